@@ -1,0 +1,137 @@
+"""CPU oracle for group-wise INT4 quantization and the W4A16 linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library
+never loads it and shares no code with it; the C source `q4_oracle.c` holds
+the arithmetic, and this module only marshals numpy arrays into it.
+
+Every function cites the passage it follows in `q4_oracle.c`.  Parity
+status: the quantizer, dequantizer, fp16 converter and reference product are
+pinned by the CPU tests (brute force, the worked example of the interview
+guide's §3, closed forms and invariants); the packing order is this
+library's own convention (the pages give none) and is pinned only by the
+brute-force unpack — parity unpinned against the pages for that layout.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+
+
+class Oracle:
+    """ctypes view of one compiled copy of the oracle library."""
+
+    def __init__(self, path):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.orc_f32_to_f16.restype = ctypes.c_uint16
+        lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.orc_f16_to_f32.restype = ctypes.c_float
+        lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_f32_to_f16_array.argtypes = [_p, _p, _c_i64]
+        lib.orc_f32_bits_range_to_f16.argtypes = [ctypes.c_uint32, _c_i64, _p]
+        lib.orc_f16_to_f32_array.argtypes = [_p, _p, _c_i64]
+        lib.orc_quantize_group.argtypes = [_p, _c_i64, ctypes.c_int, ctypes.c_int,
+                                           _p, _p, _p]
+        lib.orc_quantize_pack.restype = ctypes.c_int
+        lib.orc_quantize_pack.argtypes = [_p, _c_i64, _c_i64, _c_i32, _c_i32,
+                                          _p, _p, _p, _p]
+        lib.orc_dequant.argtypes = [_p, _p, _p, _c_i64, _c_i64, _c_i32, _p]
+        lib.orc_linear_ref.argtypes = [_p, _p, _c_i64, _c_i64, _c_i64, _p, _p]
+        self.lib = lib
+
+    # -- binary32 <-> binary16 ------------------------------------------------
+    def f32_to_f16(self, a):
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.orc_f32_to_f16_array(a.ctypes.data, out.ctypes.data, a.size)
+        return out
+
+    def f32_bits_range_to_f16(self, first, count):
+        out = np.empty(count, dtype=np.uint16)
+        self.lib.orc_f32_bits_range_to_f16(first, count, out.ctypes.data)
+        return out
+
+    def f16_to_f32(self, h):
+        h = np.ascontiguousarray(h, dtype=np.uint16)
+        out = np.empty(h.shape, dtype=np.float32)
+        self.lib.orc_f16_to_f32_array(h.ctypes.data, out.ctypes.data, h.size)
+        return out
+
+    # -- quantization ----------------------------------------------------------
+    def quantize_group(self, v, bits=4, symmetric=False):
+        """One group -> (fp32 scale, integer zero-point, int32 codes)."""
+        v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+        s = np.zeros(1, dtype=np.float32)
+        z = np.zeros(1, dtype=np.int32)
+        q = np.empty(v.size, dtype=np.int32)
+        self.lib.orc_quantize_group(v.ctypes.data, v.size, bits, int(bool(symmetric)),
+                                    s.ctypes.data, z.ctypes.data, q.ctypes.data)
+        return s[0], int(z[0]), q
+
+    def quantize_pack(self, w, group_size=128, symmetric=False):
+        """W fp32 [n_out][n_in] -> (packed u32 [n_out][n_in/8], scales fp16 bits,
+        zeros fp16 bits [n_out][n_in/g], fp32 scales before storage)."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        n_out, n_in = w.shape
+        g = n_in // group_size
+        packed = np.empty((n_out, n_in // 8), dtype=np.uint32)
+        scales = np.empty((n_out, g), dtype=np.uint16)
+        zeros = np.empty((n_out, g), dtype=np.uint16)
+        s32 = np.empty((n_out, g), dtype=np.float32)
+        rc = self.lib.orc_quantize_pack(w.ctypes.data, n_out, n_in, group_size,
+                                        int(bool(symmetric)), packed.ctypes.data,
+                                        scales.ctypes.data, zeros.ctypes.data,
+                                        s32.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected shape {w.shape} with group_size {group_size}")
+        return packed, scales, zeros, s32
+
+    def dequant(self, packed, scales, zeros, group_size):
+        """-> w' fp32 [n_out][n_in], w' = s * (q - z)."""
+        packed = np.ascontiguousarray(packed, dtype=np.uint32)
+        scales = np.ascontiguousarray(scales, dtype=np.uint16)
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+        n_out, words = packed.shape
+        n_in = words * 8
+        out = np.empty((n_out, n_in), dtype=np.float32)
+        self.lib.orc_dequant(packed.ctypes.data, scales.ctypes.data, zeros.ctypes.data,
+                             n_out, n_in, group_size, out.ctypes.data)
+        return out
+
+    def linear_ref(self, x_f16_bits, w_deq):
+        """x fp16 bits [m][n_in], w' fp32 [n_out][n_in] -> (y, a) float64 [m][n_out]
+        with y = x w'^T and a = |x| |w'|^T, accumulated in binary64."""
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        w = np.ascontiguousarray(w_deq, dtype=np.float32)
+        m, n_in = x.shape
+        n_out = w.shape[0]
+        assert w.shape[1] == n_in
+        y = np.empty((m, n_out), dtype=np.float64)
+        a = np.empty((m, n_out), dtype=np.float64)
+        self.lib.orc_linear_ref(x.ctypes.data, w.ctypes.data, m, n_out, n_in,
+                                y.ctypes.data, a.ctypes.data)
+        return y, a
+
+    def linear_from_packed(self, x_f16_bits, packed, scales, zeros, group_size):
+        """Dequantize, then take the reference product (two plain steps)."""
+        return self.linear_ref(x_f16_bits, self.dequant(packed, scales, zeros, group_size))
+
+
+_DEFAULT = None
+
+
+def load():
+    """The oracle built from oracle/q4_oracle.c (built with gcc if absent)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _DEFAULT = Oracle(_build.LIB)
+    return _DEFAULT

@@ -1,0 +1,278 @@
+/*
+ * q4_oracle.c -- CPU oracle for group-wise INT4 weight quantization and the
+ * W4A16 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct
+ * definition that the GPU library is checked against.  Only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg load it.  It shares no
+ * code, header, table or constant generator with the HIP library, and the
+ * HIP library never loads it.
+ *
+ * Sources (cited by page title and section):
+ *   [Guide]  "27届大模型面试准备十九 模型量化全攻略 -- INT8/INT4、GPTQ、AWQ、
+ *            SmoothQuant 与 KV Cache 量化" (dksg.cn)
+ *   [Path]   "从 FP32 到 INT4：大模型推理加速中的量化优化实战路径" (adg.csdn.net)
+ *   [Zero]   "从0到1：大模型量化" (pinyinjj.github.io)
+ *   [Intro]  "大模型量化技术入门：为什么我们需要量化？" (devpress.csdn.net)
+ *
+ * Precision.  The pages state the quantizer on float32 tensors ([Guide] §2.1,
+ * the quantize_tensor snippet; [Path] §2.1, the NumPy quantizers), so every
+ * quantizer step here is one IEEE binary32 operation with round-to-nearest-
+ * even.  Build with -ffp-contract=off and without fast-math so that no step
+ * is fused or reassociated.  The reference product is accumulated in binary64.
+ *
+ * Readings where the pages are silent or disagree (all listed in the design
+ * notes of the repository):
+ *   - the 1e-8 floor on s is applied before z and the codes are computed;
+ *   - z is clipped to [0, 2^b - 1] as in [Path] §2.1;
+ *   - codes are computed from the fp32 s; fp16 is the storage type of s, z;
+ *   - rounding is round-half-to-even (torch.round / np.round semantics);
+ *   - symmetric 4-bit codes q in [-8, 7] are stored offset-binary as q + 8
+ *     with a stored zero-point of 8, so dequantization is mode-agnostic;
+ *   - packing (not on the pages): element 8j+t of a row sits in bits
+ *     4t..4t+3 of 32-bit word j of that row, rows are [n_out][n_in/8].
+ *
+ * Parity status of each function is stated beside it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* binary32 <-> binary16, written from the IEEE 754 definitions.             */
+/* Pinned against numpy.float16 over every binary32 bit pattern.             */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t bits_of(float f) { uint32_t b; memcpy(&b, &f, 4); return b; }
+static float float_of(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
+
+/* Round-to-nearest-even conversion.  Subnormal halves are produced, values
+ * whose magnitude rounds past the largest half (65504) become infinity, and
+ * NaN stays NaN (payload not specified). */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t b = bits_of(f);
+    uint16_t sign = (uint16_t)((b >> 16) & 0x8000u);
+    uint32_t e8 = (b >> 23) & 0xFFu;
+    uint32_t frac = b & 0x7FFFFFu;
+
+    if (e8 == 0xFFu)                       /* inf or NaN */
+        return (uint16_t)(sign | (frac ? 0x7E00u : 0x7C00u));
+    if (e8 == 0)                           /* binary32 zero/subnormal: < 2^-126 */
+        return sign;
+
+    /* |f| = sig * 2^(e - 23) with a 24-bit significand. */
+    int e = (int)e8 - 127;
+    uint32_t sig = frac | 0x800000u;
+
+    /* The half result is q * 2^(E - 10) for normal halves (E = max(e, -14))
+     * and q * 2^-24 for subnormal ones; both cases drop `shift` low bits. */
+    int shift = (e >= -14) ? 13 : (-1 - e);
+    if (shift > 24)                        /* below half of the least subnormal */
+        return sign;
+    uint32_t q = sig >> shift;
+    uint32_t rem = sig & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u)))
+        q += 1u;                           /* round to nearest, ties to even */
+
+    uint32_t h;
+    if (e >= -14) {
+        if (e > 15)
+            return (uint16_t)(sign | 0x7C00u);
+        /* q holds the implicit bit (0x400); a carry out of the significand
+         * moves into the exponent field, which is exactly the right result,
+         * including the step from 65504 up to infinity. */
+        h = ((uint32_t)(e + 14) << 10) + q;
+        if (h >= 0x7C00u)
+            h = 0x7C00u;
+    } else {
+        h = q;                              /* 0x400 here is the least normal */
+    }
+    return (uint16_t)(sign | h);
+}
+
+/* Exact widening. */
+float orc_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+    uint32_t e5 = ((uint32_t)h >> 10) & 0x1Fu;
+    uint32_t frac = (uint32_t)h & 0x3FFu;
+    if (e5 == 0) {
+        float mag = (float)frac * 0x1p-24f;           /* exact */
+        return float_of(bits_of(mag) | sign);
+    }
+    if (e5 == 0x1Fu)
+        return float_of(sign | 0x7F800000u | (frac << 13));
+    return float_of(sign | ((e5 - 15u + 127u) << 23) | (frac << 13));
+}
+
+void orc_f32_to_f16_array(const float *src, uint16_t *dst, int64_t n)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        dst[i] = orc_f32_to_f16(src[i]);
+}
+
+/* Converts the binary32 values whose bit patterns are first, first+1, ...,
+ * first+count-1 (used by the exhaustive converter test). */
+void orc_f32_bits_range_to_f16(uint32_t first, int64_t count, uint16_t *dst)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++)
+        dst[i] = orc_f32_to_f16(float_of(first + (uint32_t)i));
+}
+
+void orc_f16_to_f32_array(const uint16_t *src, float *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        dst[i] = orc_f16_to_f32(src[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Uniform affine quantization of one group.                                 */
+/* [Guide] §2.1 (q = clamp(round(x/s) + z, qmin, qmax); min-max calibration: */
+/* symmetric s = max|x| / (2^(b-1) - 1), asymmetric s = (max - min)/(2^b-1), */
+/* z = round(-min/s); s floored at 1e-8); [Path] §2.1 (z clipped to         */
+/* [0, 2^b - 1], symmetric codes clipped to [-2^(b-1), 2^(b-1) - 1]);       */
+/* [Intro] §2.2 and [Zero] §2 (Q = round(X/scale) + zero_point).             */
+/* Pinned by brute force over all codes, the worked per-tensor example of    */
+/* [Guide] §3, the s/2 bound, idempotence, grid-exact and constant groups.   */
+/* ------------------------------------------------------------------------ */
+
+static float clampf(float v, float lo, float hi)
+{
+    if (v < lo) v = lo;
+    if (v > hi) v = hi;
+    return v;
+}
+
+/* v[0..n) -> fp32 scale *s, integer zero-point *z and integer codes q[].
+ * Asymmetric codes lie in [0, 2^b - 1]; symmetric codes in
+ * [-2^(b-1), 2^(b-1) - 1] with z = 0. */
+void orc_quantize_group(const float *v, int64_t n, int bits, int symmetric,
+                        float *s_out, int32_t *z_out, int32_t *q)
+{
+    if (symmetric) {
+        const float qmax = (float)((1 << (bits - 1)) - 1);
+        const float qmin = -(float)(1 << (bits - 1));
+        float amax = 0.0f;
+        for (int64_t i = 0; i < n; i++)
+            if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+        float s = amax / qmax;
+        if (s < 1e-8f) s = 1e-8f;
+        for (int64_t i = 0; i < n; i++)
+            q[i] = (int32_t)clampf(rintf(v[i] / s), qmin, qmax);
+        *s_out = s;
+        *z_out = 0;
+    } else {
+        const float qmax = (float)((1 << bits) - 1);
+        float mn = v[0], mx = v[0];
+        for (int64_t i = 1; i < n; i++) {
+            if (v[i] < mn) mn = v[i];
+            if (v[i] > mx) mx = v[i];
+        }
+        float s = (mx - mn) / qmax;
+        if (s < 1e-8f) s = 1e-8f;
+        int32_t z = (int32_t)clampf(rintf(-mn / s), 0.0f, qmax);
+        for (int64_t i = 0; i < n; i++)
+            q[i] = (int32_t)clampf(rintf(v[i] / s) + (float)z, 0.0f, qmax);
+        *s_out = s;
+        *z_out = z;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-group INT4 quantization of W[n_out][n_in] along the input dimension,  */
+/* fp16 storage of s and z, and packing of 8 codes per 32-bit word.          */
+/* [Guide] §2.2 (W[out_features, in_features], one scale per group of 128    */
+/* input elements per output channel, fp16 scale); [Zero] §3.1 (each block   */
+/* keeps its own S and Z); [Path] §2.2 (group_size 128 / 64).                */
+/* The packing order is this library's convention; it is pinned only by the  */
+/* brute-force unpack (parity unpinned against the pages, which give none).  */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_pack(const float *w, int64_t n_out, int64_t n_in,
+                      int32_t group_size, int32_t symmetric,
+                      uint32_t *packed, uint16_t *scales, uint16_t *zeros,
+                      float *s_fp32 /* may be NULL */)
+{
+    if (group_size <= 0 || group_size > 1024 || n_in % group_size != 0 ||
+        n_in % 8 != 0)
+        return 1;
+    const int64_t groups = n_in / group_size;
+
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_out; n++) {
+        int32_t codes[1024];
+        uint32_t *row = packed + n * (n_in / 8);
+        memset(row, 0, (size_t)(n_in / 8) * sizeof(uint32_t));
+        for (int64_t j = 0; j < groups; j++) {
+            const float *v = w + n * n_in + j * group_size;
+            float s;
+            int32_t z;
+            orc_quantize_group(v, group_size, 4, symmetric, &s, &z, codes);
+            int32_t z_store = symmetric ? 8 : z;
+            for (int64_t t = 0; t < group_size; t++) {
+                uint32_t u = (uint32_t)(symmetric ? codes[t] + 8 : codes[t]);
+                int64_t k = j * group_size + t;
+                row[k / 8] |= u << (4 * (k % 8));
+            }
+            scales[n * groups + j] = orc_f32_to_f16(s);
+            zeros[n * groups + j] = orc_f32_to_f16((float)z_store);
+            if (s_fp32)
+                s_fp32[n * groups + j] = s;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantization w' = s * (q - z) in float32.                               */
+/* [Guide] §2.1 (x_hat = s * (q - z); dequantize_tensor returns float32);    */
+/* [Zero] §2 (f' = S * (q - Z)).  The product of an fp16 scale and an        */
+/* integer in [-15, 15] is exact in binary32.                                */
+/* ------------------------------------------------------------------------ */
+void orc_dequant(const uint32_t *packed, const uint16_t *scales,
+                 const uint16_t *zeros, int64_t n_out, int64_t n_in,
+                 int32_t group_size, float *out)
+{
+    const int64_t groups = n_in / group_size;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_out; n++) {
+        for (int64_t k = 0; k < n_in; k++) {
+            uint32_t word = packed[n * (n_in / 8) + k / 8];
+            int32_t u = (int32_t)((word >> (4 * (k % 8))) & 0xFu);
+            float s = orc_f16_to_f32(scales[n * groups + k / group_size]);
+            int32_t z = (int32_t)orc_f16_to_f32(zeros[n * groups + k / group_size]);
+            out[n * n_in + k] = s * (float)(u - z);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Reference product of the linear layer on the dequantized weights:         */
+/* y[m][n] = sum_k x[m][k] * w'[n][k] and a[m][n] = sum_k |x[m][k] w'[n][k]| */
+/* in binary64 (each product is exact there).  [Guide] §2.2 (W is           */
+/* [out_features, in_features]) and §2.3 (W4A16: INT4 weights, FP16          */
+/* activations, weights dequantized before the product).                    */
+/* Pinned against numpy float64 matmul and one-hot inputs.                   */
+/* ------------------------------------------------------------------------ */
+void orc_linear_ref(const uint16_t *x_f16, const float *w_deq,
+                    int64_t m, int64_t n_out, int64_t n_in,
+                    double *y, double *a)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_out; n++) {
+        for (int64_t i = 0; i < m; i++) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t k = 0; k < n_in; k++) {
+                double p = (double)orc_f16_to_f32(x_f16[i * n_in + k])
+                         * (double)w_deq[n * n_in + k];
+                acc += p;
+                acc_abs += fabs(p);
+            }
+            y[i * n_out + n] = acc;
+            a[i * n_out + n] = acc_abs;
+        }
+    }
+}

@@ -1,0 +1,358 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each pin takes an `oracle.Oracle` and raises AssertionError when the oracle
+disagrees with what the pages or the mathematics fix.  The same pins run
+against deliberately broken copies of the oracle (tests/test_oracle_mutants.py)
+to show that a plausible mistake anywhere in it is caught.
+"""
+import json
+import os
+
+import numpy as np
+import torch
+
+from brute import check_matrix
+from w4a16_dequant_gemv_amd import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _f16_bits_to_f32(h):
+    return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def _f16_bits(a_f32):
+    """fp16 bit patterns by torch's CPU conversion (hardware F16C, IEEE RNE)."""
+    t = torch.from_numpy(np.ascontiguousarray(a_f32, dtype=np.float32)).half()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Worked example: the interview guide's §3, per-tensor symmetric INT8.
+# ---------------------------------------------------------------------------
+def pin_worked_example(orc, quick=False):
+    g = _golden("worked_example.json")
+    rng = np.random.default_rng(11)
+    x = rng.uniform(-3, 3, size=4096).astype(np.float32)       # normal channels
+    x[17] = g["max_abs"]                                         # the outlier channel
+    x[901] = -63.0
+    x[5] = g["x"]
+    s, z, q = orc.quantize_group(x, bits=g["bits"], symmetric=g["symmetric"])
+    tol = 0.5 * 10.0 ** (-g["scale_printed_digits"])
+    assert abs(float(s) - g["scale_printed"]) <= tol, f"scale {s} vs printed {g['scale_printed']}"
+    assert z == 0
+    assert int(q[5]) == g["q"], f"q(0.5) = {q[5]}"
+    assert int(q[17]) == 2 ** (g["bits"] - 1) - 1, "max|x| must map to the top code"
+    x_hat = float(s) * (int(q[5]) - z)
+    assert abs(x_hat - g["x_hat_printed"]) <= tol, f"x_hat {x_hat}"
+    rel = abs(x_hat - g["x"]) / g["x"] * 100
+    assert round(rel) == g["rel_error_percent_printed"], f"error {rel}%"
+    # small channels are crushed onto few codes, as the page describes
+    assert set(np.unique(q[np.abs(x) < 1.0])) <= {-1, 0, 1}
+
+
+# ---------------------------------------------------------------------------
+# Brute force over every code on 2x256 matrices.
+# ---------------------------------------------------------------------------
+def _small_cases():
+    cases = []
+    w = synthetic.normal_weight(2, 256, seed=21, std=0.02, n_outlier_cols=3)
+    cases.append(w)
+    cases.append(synthetic.student_t_weight(2, 256, seed=22, group_size=32,
+                                            const_frac=0.0, zero_frac=0.0))
+    rng = np.random.default_rng(23)
+    u = rng.uniform(-1, 1, size=(2, 256)).astype(np.float32)
+    u[0, :128] = np.abs(u[0, :128]) + 0.25          # all-positive groups
+    u[1, 128:] = -np.abs(u[1, 128:]) - 0.25         # all-negative groups
+    cases.append(u)
+    return cases
+
+
+def pin_brute_force(orc, quick=False):
+    for ci, w in enumerate(_small_cases()):
+        for g in (32, 128):
+            for sym in (False, True):
+                packed, scales, zeros, s32 = orc.quantize_pack(w, g, sym)
+                try:
+                    check_matrix(w, packed, scales, zeros, s32, g, sym)
+                except AssertionError as e:
+                    raise AssertionError(f"case {ci} g={g} sym={sym}: {e}") from None
+
+
+# ---------------------------------------------------------------------------
+# Exact ties round to even (the pages round with torch.round / np.round).
+# ---------------------------------------------------------------------------
+def pin_ties_to_even(orc, quick=False):
+    # range [-7, 8] gives s = 1 exactly and z = 7; w/s is then w itself
+    vals = [-7.0, 8.0, 0.5, 1.5, 2.5, -0.5, -1.5, 3.5, -2.5, 4.5] + [0.0] * 22
+    w = np.array([vals], dtype=np.float32)
+    packed, scales, zeros, s32 = orc.quantize_pack(w, 32, False)
+    assert float(s32[0, 0]) == 1.0 and float(_f16_bits_to_f32(zeros)[0, 0]) == 7.0
+    codes = [(int(packed[0, k // 8]) >> (4 * (k % 8))) & 0xF for k in range(32)]
+    want = [round(v) + 7 for v in vals]             # Python's round: half to even
+    assert codes == want, f"tie codes {codes[:10]} != {want[:10]}"
+    # symmetric: max|w| = 7 gives s = 1, ties on the signed codes
+    vals_s = [7.0, -6.5, 0.5, 1.5, 2.5, -0.5, -3.5, 5.5] + [0.0] * 24
+    w = np.array([vals_s], dtype=np.float32)
+    packed, scales, zeros, s32 = orc.quantize_pack(w, 32, True)
+    assert float(s32[0, 0]) == 1.0
+    codes = [(int(packed[0, k // 8]) >> (4 * (k % 8))) & 0xF for k in range(32)]
+    assert codes == [round(v) + 8 for v in vals_s], f"symmetric tie codes {codes[:8]}"
+
+
+# ---------------------------------------------------------------------------
+# Zero-point clipping to [0, 15] for one-signed groups.
+# ---------------------------------------------------------------------------
+def pin_zero_clip(orc, quick=False):
+    w = np.empty((2, 32), dtype=np.float32)
+    w[0] = np.linspace(0.5, 2.0, 32)
+    w[1] = np.linspace(-2.0, -0.5, 32)
+    packed, scales, zeros, s32 = orc.quantize_pack(w, 32, False)
+    z = _f16_bits_to_f32(zeros)[:, 0]
+    assert z[0] == 0.0, f"all-positive group: zero-point {z[0]} should clip to 0"
+    assert z[1] == 15.0, f"all-negative group: zero-point {z[1]} should clip to 15"
+
+
+# ---------------------------------------------------------------------------
+# Reconstruction bound |w - w'| <= s/2 (+ fp16 storage slack).
+# ---------------------------------------------------------------------------
+def _bound_cases(quick):
+    rows = 32 if quick else 128
+    return [
+        ("normal+outliers", synthetic.normal_weight(rows, 4096, seed=31, std=0.02,
+                                                    n_outlier_cols=8)),
+        ("student-t", synthetic.student_t_weight(rows, 2048, seed=32, group_size=128,
+                                                 const_frac=0.0, zero_frac=0.0)),
+    ]
+
+
+def pin_reconstruction_bound(orc, quick=False):
+    for name, w in _bound_cases(quick):
+        for g in (32, 128):
+            for sym in (False, True):
+                packed, scales, zeros, s32 = orc.quantize_pack(w, g, sym)
+                wd = orc.dequant(packed, scales, zeros, g)
+                n_out, n_in = w.shape
+                G = n_in // g
+                s = s32.astype(np.float64).repeat(g, axis=1)
+                sh = _f16_bits_to_f32(scales).astype(np.float64).repeat(g, axis=1)
+                grp = w.reshape(n_out, G, g)
+                if sym:
+                    ok = (np.abs(grp).max(axis=2) / 7 > 1e-7)
+                    cmax = 8
+                else:
+                    mn, mx = grp.min(axis=2), grp.max(axis=2)
+                    ok = (mn <= 0) & (mx >= 0) & ((mx - mn) / 15 > 1e-7)
+                    cmax = 15
+                ok = ok.repeat(g, axis=1)
+                err = np.abs(w.astype(np.float64) - wd.astype(np.float64))
+                bound = s * (0.5 + 2.0 ** -18) + cmax * np.abs(s - sh)
+                bad = ok & (err > bound)
+                assert not bad.any(), (f"{name} g={g} sym={sym}: |w-w'| exceeds s/2 at "
+                                       f"{np.argwhere(bad)[:3].tolist()}")
+                assert np.isfinite(wd).all()
+
+
+# ---------------------------------------------------------------------------
+# Quantize o dequantize o quantize == quantize.
+# ---------------------------------------------------------------------------
+def _codes(packed):
+    shifts = (4 * np.arange(8, dtype=np.uint32))
+    return ((packed[..., None] >> shifts) & 0xF).reshape(packed.shape[0], -1)
+
+
+def pin_idempotence(orc, quick=False):
+    for name, w in _bound_cases(quick):
+        for g in (32, 128):
+            for sym in (False, True):
+                p1, s1, z1, _ = orc.quantize_pack(w, g, sym)
+                wd = orc.dequant(p1, s1, z1, g)
+                p2, s2, z2, _ = orc.quantize_pack(wd, g, sym)
+                n_out, n_in = w.shape
+                G = n_in // g
+                c1 = _codes(p1).reshape(n_out, G, g)
+                c2 = _codes(p2).reshape(n_out, G, g)
+                sh = _f16_bits_to_f32(s1)
+                if sym:
+                    sel = sh > 0
+                else:
+                    sel = (c1.min(axis=2) == 0) & (c1.max(axis=2) == 15) & (sh > 0)
+                assert sel.mean() > 0.5, f"{name} g={g}: too few qualifying groups"
+                same = (c1 == c2).all(axis=2) & (s1 == s2) & (z1 == z2)
+                bad = sel & ~same
+                assert not bad.any(), (f"{name} g={g} sym={sym}: Q(D(Q(W))) != Q(W) in "
+                                       f"{int(bad.sum())} groups, first {np.argwhere(bad)[0].tolist()}")
+
+
+# ---------------------------------------------------------------------------
+# Groups that lie exactly on a grid come back exactly.
+# ---------------------------------------------------------------------------
+def pin_grid_exact(orc, quick=False):
+    rng = np.random.default_rng(41)
+    g, rows = 128, 16
+    w = np.empty((rows, 4 * g), dtype=np.float32)
+    expect = []
+    for r in range(rows):
+        for j in range(4):
+            s = np.float32(np.float16(rng.uniform(1e-3, 0.2)))       # fp16-exact scale
+            z = int(rng.integers(0, 16))
+            u = rng.integers(0, 16, size=g)
+            u[rng.integers(0, g)] = 0
+            u[rng.integers(0, g)] = 15
+            w[r, j * g:(j + 1) * g] = s * (u - z).astype(np.float32)
+            expect.append((r, j, s, z, u))
+    packed, scales, zeros, s32 = orc.quantize_pack(w, g, False)
+    codes = _codes(packed).reshape(rows, 4, g)
+    sh = _f16_bits_to_f32(scales)
+    zh = _f16_bits_to_f32(zeros)
+    for r, j, s, z, u in expect:
+        assert sh[r, j] == s, f"row {r} group {j}: scale {sh[r, j]} != {s}"
+        assert zh[r, j] == z, f"row {r} group {j}: zero {zh[r, j]} != {z}"
+        assert np.array_equal(codes[r, j], u), f"row {r} group {j}: codes differ"
+    wd = orc.dequant(packed, scales, zeros, g)
+    assert np.array_equal(wd.view(np.uint32), w.view(np.uint32)), "grid-exact W not reproduced bitwise"
+
+
+# ---------------------------------------------------------------------------
+# Constant groups (max == min): no NaN or Inf, closed-form codes.
+# ---------------------------------------------------------------------------
+def pin_constant_groups(orc, quick=False):
+    g = 32
+    consts = [0.75, -0.75, 0.0, -0.0, 3e-9, 2e-8]
+    w = np.repeat(np.array(consts, dtype=np.float32)[:, None], g, axis=1)
+    packed, scales, zeros, s32 = orc.quantize_pack(w, g, False)
+    codes = _codes(packed)
+    sh = _f16_bits_to_f32(scales)[:, 0]
+    zh = _f16_bits_to_f32(zeros)[:, 0]
+    # s floors at 1e-8 (which rounds to fp16 zero); then w/s decides the code:
+    # c = 0.75 -> 15 with z 0; c = -0.75 -> 0 with z 15; c = +-0 -> 0 with z 0;
+    # c = 3e-9 -> rint(0.3) = 0; c = 2e-8 -> rint(2) = 2 with z 0.
+    assert np.all(s32[:, 0] == np.float32(1e-8)) and np.all(sh == 0.0)
+    want = [(15, 0), (0, 15), (0, 0), (0, 0), (0, 0), (2, 0)]
+    for i, (u, z) in enumerate(want):
+        assert np.all(codes[i] == u) and zh[i] == z, f"constant {consts[i]}: codes {codes[i][0]}, z {zh[i]}"
+    wd = orc.dequant(packed, scales, zeros, g)
+    assert np.all(wd == 0.0) and np.isfinite(wd).all()
+    # symmetric: a nonzero constant is reconstructed through s = |c|/7
+    packed, scales, zeros, s32 = orc.quantize_pack(w, g, True)
+    codes = _codes(packed)
+    assert np.all(codes[0] == 15) and np.all(codes[1] == 1) and np.all(codes[2] == 8)
+    wd = orc.dequant(packed, scales, zeros, g)
+    assert abs(wd[0, 0] - 0.75) < 1e-3 and abs(wd[1, 0] + 0.75) < 1e-3 and wd[2, 0] == 0.0
+    assert np.isfinite(wd).all()
+
+
+# ---------------------------------------------------------------------------
+# Storage accounting: 4.25 bits per weight at g=128, metadata shares.
+# ---------------------------------------------------------------------------
+def pin_storage_accounting(orc, quick=False):
+    entries = _golden("storage_accounting.json")["entries"]
+    w = synthetic.normal_weight(8, 4096, seed=51)
+    for e in entries:
+        if "effective_bits_printed" in e:
+            g = e["group_size"]
+            packed, scales, zeros, _ = orc.quantize_pack(w, g, False)
+            assert scales.shape[1] == e["scales_per_output_channel_printed"]
+            bits = 8 * (packed.nbytes + scales.nbytes + zeros.nbytes) / w.size
+            assert abs(bits - e["effective_bits_printed"]) < 1e-9, f"{bits} bits/weight"
+        if "metadata_percent_printed" in e:
+            g = e["group_size"]
+            packed, scales, zeros, _ = orc.quantize_pack(w, g, False)
+            share = 100.0 * scales.nbytes / packed.nbytes
+            assert abs(share - e["metadata_percent_printed"]) < 0.05 + 1e-9, f"{share}%"
+        if "int4_gb_printed" in e:
+            packed, _, _, _ = orc.quantize_pack(w, 128, False)
+            gb = e["params"] * (packed.nbytes / w.size) / 1e9
+            assert gb == e["int4_gb_printed"]
+
+
+# ---------------------------------------------------------------------------
+# binary32 -> binary16 against torch's hardware conversion, every pattern.
+# ---------------------------------------------------------------------------
+def pin_f16_converter(orc, quick=False):
+    chunk = 1 << 26
+    if quick:
+        rng = np.random.default_rng(61)
+        starts = [int(x) << 20 for x in rng.choice(1 << 12, size=16, replace=False)]
+        starts += [0x33000000, 0x387FF000, 0x477FE000, 0x7F7FF000]
+        count = 1 << 16
+    else:
+        starts = list(range(0, 1 << 32, chunk))
+        count = chunk
+    for first in starts:
+        bits = np.arange(first, first + count, dtype=np.uint64).astype(np.uint32)
+        f = bits.view(np.float32)
+        got = orc.f32_bits_range_to_f16(first, count)
+        want = _f16_bits(f)
+        nan = np.isnan(f)
+        bad = (got != want) & ~nan
+        assert not bad.any(), (f"fp32 {hex(int(bits[bad][0]))}: {hex(int(got[bad][0]))} "
+                               f"vs {hex(int(want[bad][0]))}")
+        gh = got[nan]
+        assert np.all(((gh & 0x7C00) == 0x7C00) & ((gh & 0x3FF) != 0)), "NaN must stay NaN"
+    # widening: every half pattern, exact
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.f16_to_f32(h)
+    want = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(got.view(np.uint32)[~nan], want.view(np.uint32)[~nan])
+    assert np.isnan(got[nan]).all()
+
+
+# ---------------------------------------------------------------------------
+# Dequantization against an independent unpack with numpy's fp16.
+# ---------------------------------------------------------------------------
+def pin_dequant(orc, quick=False):
+    rng = np.random.default_rng(71)
+    n_out, n_in, g = 24, 512, 64
+    packed = rng.integers(0, 1 << 32, size=(n_out, n_in // 8), dtype=np.uint64).astype(np.uint32)
+    s = rng.uniform(0, 0.1, size=(n_out, n_in // g)).astype(np.float16)
+    s[0, 0] = 0.0
+    s[1, 1] = np.float16(6e-8)                    # fp16 subnormal
+    z = rng.integers(0, 16, size=(n_out, n_in // g)).astype(np.float16)
+    got = orc.dequant(packed, s.view(np.uint16), z.view(np.uint16), g)
+    codes = _codes(packed).astype(np.int64)
+    want = (s.astype(np.float32).repeat(g, axis=1)
+            * (codes - z.astype(np.int64).repeat(g, axis=1)).astype(np.float32))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "dequant differs bitwise"
+
+
+# ---------------------------------------------------------------------------
+# Reference product against a numpy float64 matmul, one-hot and zero inputs.
+# ---------------------------------------------------------------------------
+def pin_linear_ref(orc, quick=False):
+    rng = np.random.default_rng(81)
+    m, n_out, n_in = 5, 96, 1024
+    x = rng.standard_normal((m, n_in)).astype(np.float16)
+    wd = (rng.standard_normal((n_out, n_in)) * 0.02).astype(np.float32)
+    y, a = orc.linear_ref(x.view(np.uint16), wd)
+    xd = x.astype(np.float64)
+    want = xd @ wd.astype(np.float64).T
+    want_a = np.abs(xd) @ np.abs(wd.astype(np.float64)).T
+    assert np.allclose(y, want, rtol=0, atol=1e-12 * want_a.max())
+    assert np.allclose(a, want_a, rtol=1e-13, atol=0)
+    # one-hot x picks one column of w' exactly
+    k = 333
+    onehot = np.zeros((1, n_in), dtype=np.float16)
+    onehot[0, k] = 1.0
+    y1, _ = orc.linear_ref(onehot.view(np.uint16), wd)
+    assert np.array_equal(y1[0], wd[:, k].astype(np.float64))
+    # a non-symmetric x and w catch a transposed operand
+    x2 = np.zeros((2, n_in), dtype=np.float16)
+    x2[1, 7] = 2.0
+    y2, _ = orc.linear_ref(x2.view(np.uint16), wd)
+    assert np.all(y2[0] == 0) and np.array_equal(y2[1], 2.0 * wd[:, 7].astype(np.float64))
+    y0, a0 = orc.linear_ref(x.view(np.uint16), np.zeros_like(wd))
+    assert np.all(y0 == 0) and np.all(a0 == 0)
+
+
+ALL_PINS = [
+    pin_worked_example, pin_brute_force, pin_ties_to_even, pin_zero_clip,
+    pin_reconstruction_bound, pin_idempotence, pin_grid_exact, pin_constant_groups,
+    pin_storage_accounting, pin_f16_converter, pin_dequant, pin_linear_ref,
+]

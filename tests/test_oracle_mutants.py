@@ -1,0 +1,70 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a copy of oracle/q4_oracle.c with one plausible slip (a wrong
+rounding, sign, index, clamp, nibble order, divisor ...), built with the same
+flags into a temporary directory.  Everything happens on the CPU.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from pins import ALL_PINS
+
+MUTANTS = {
+    "round_half_up": ("rintf(v[i] / s) + (float)z", "floorf(v[i] / s + 0.5f) + (float)z"),
+    "zero_point_sign": ("rintf(-mn / s)", "rintf(mn / s)"),
+    "zero_point_unclipped": ("(int32_t)clampf(rintf(-mn / s), 0.0f, qmax)",
+                             "(int32_t)rintf(-mn / s)"),
+    "no_scale_floor_asym": ("        float s = (mx - mn) / qmax;\n        if (s < 1e-8f) s = 1e-8f;",
+                            "        float s = (mx - mn) / qmax;"),
+    "asym_divisor_2b": ("float s = (mx - mn) / qmax;", "float s = (mx - mn) / (qmax + 1.0f);"),
+    "sym_divisor_2b_minus_1": ("const float qmax = (float)((1 << (bits - 1)) - 1);",
+                               "const float qmax = (float)((1 << bits) - 1);"),
+    "sym_offset_7": ("codes[t] + 8 : codes[t]", "codes[t] + 7 : codes[t]"),
+    "nibble_order_reversed": ("row[k / 8] |= u << (4 * (k % 8));",
+                              "row[k / 8] |= u << (4 * (7 - k % 8));"),
+    "min_init_zero": ("float mn = v[0], mx = v[0];", "float mn = 0.0f, mx = v[0];"),
+    "dequant_sign": ("out[n * n_in + k] = s * (float)(u - z);",
+                     "out[n * n_in + k] = s * (float)(z - u);"),
+    "dequant_group_index": ("float s = orc_f16_to_f32(scales[n * groups + k / group_size]);",
+                            "float s = orc_f16_to_f32(scales[n * groups + (k / group_size + 1) % groups]);"),
+    "dequant_nibble_index": ("int32_t u = (int32_t)((word >> (4 * (k % 8))) & 0xFu);",
+                             "int32_t u = (int32_t)((word >> (4 * ((k + 1) % 8))) & 0xFu);"),
+    "f16_truncate": ("if (rem > half || (rem == half && (q & 1u)))", "if (0)"),
+    "f16_ties_away": ("if (rem > half || (rem == half && (q & 1u)))", "if (rem >= half)"),
+    "f16_subnormal_scale": ("float mag = (float)frac * 0x1p-24f;", "float mag = (float)frac * 0x1p-23f;"),
+    "linear_reversed_k": ("(double)orc_f16_to_f32(x_f16[i * n_in + k])",
+                          "(double)orc_f16_to_f32(x_f16[i * n_in + (n_in - 1 - k)])"),
+    "linear_abs_dropped": ("acc_abs += fabs(p);", "acc_abs += p;"),
+    "linear_row_swap": ("y[i * n_out + n] = acc;", "y[i * n_out + (n_out - 1 - n)] = acc;"),
+}
+
+
+def _failing_pins(orc):
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc, quick=True)
+        except AssertionError:
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(obuild.SRC, encoding="utf-8").read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique in the oracle source"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new), encoding="utf-8")
+    lib = obuild.build(str(path), str(tmp_path / f"lib_{name}.so"), extra_flags=["-w"])
+    failed = _failing_pins(oracle.Oracle(lib))
+    assert failed, f"mutant {name} passes every pin"
+
+
+def test_unmutated_copy_passes_quick_pins(tmp_path):
+    lib = obuild.build(obuild.SRC, str(tmp_path / "lib_copy.so"))
+    assert _failing_pins(oracle.Oracle(lib)) == []
+    assert os.path.exists(lib)

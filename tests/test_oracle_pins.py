@@ -1,0 +1,9 @@
+"""The CPU oracle against what the pages and the mathematics fix."""
+import pytest
+
+from pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(orc, pin):
+    pin(orc, quick=False)

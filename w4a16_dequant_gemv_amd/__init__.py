@@ -1,0 +1,22 @@
+"""W4A16 group-wise INT4 weight quantization and fused-dequant GEMV/GEMM for
+AMD Instinct MI355X (gfx950).
+
+The arithmetic runs in the HIP library `libw4a16.so` behind a C ABI
+(`include/w4a16.h`); this package only marshals torch tensors into it.
+Submodules load lazily so that the seeded input generators in `synthetic`
+can be imported on machines without the library.
+"""
+import importlib
+
+__all__ = ["quantize_pack", "dequant", "gemv", "gemm", "linear", "QuantizedWeight",
+           "W4A16Error", "synthetic"]
+
+
+def __getattr__(name):
+    if name in ("quantize_pack", "dequant", "gemv", "gemm", "linear",
+                "QuantizedWeight", "W4A16Error"):
+        api = importlib.import_module(".api", __name__)
+        return getattr(api, name)
+    if name == "synthetic":
+        return importlib.import_module(".synthetic", __name__)
+    raise AttributeError(name)

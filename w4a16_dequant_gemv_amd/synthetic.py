@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs shaped like the models the pages discuss.
+
+This module only draws random numbers; it holds none of the quantization or
+matrix arithmetic.  Both the GPU path and the CPU oracle take its outputs as
+plain arrays, so it is the only code the two sides share.
+
+Distributions follow the workloads:
+  * weights W[out, in] ~ N(0, std) in float32, with a small set of input
+    columns scaled by 50 to stand in for outlier channels (the pages put
+    such channels at about 0.1 % and 50-100x the typical range);
+  * heavy-tailed weights 0.02 * Student-t(3) with a share of constant
+    groups (max == min) and of all-zero groups;
+  * activations x ~ N(0, 1), rounded once to fp16.
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+OUTLIER_SCALE = 50.0
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def outlier_columns(n_in, count, seed):
+    """The input-dimension indices scaled as outlier channels."""
+    if count <= 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.sort(_rng(seed + 7_000_003).choice(n_in, size=count, replace=False))
+
+
+def normal_weight(n_out, n_in, seed, std=0.02, n_outlier_cols=0):
+    """float32 [n_out][n_in] ~ N(0, std), `n_outlier_cols` columns x50."""
+    w = _rng(seed).standard_normal((n_out, n_in), dtype=np.float32)
+    w *= np.float32(std)
+    cols = outlier_columns(n_in, n_outlier_cols, seed)
+    if cols.size:
+        w[:, cols] *= np.float32(OUTLIER_SCALE)
+    return w
+
+
+def student_t_weight(n_out, n_in, seed, group_size, nu=3.0, scale=0.02,
+                     const_frac=0.01, zero_frac=0.001):
+    """float32 [n_out][n_in] = scale * t(nu); a `const_frac` share of groups is
+    set to the group's first value, a `zero_frac` share to exactly 0."""
+    rng = _rng(seed)
+    w = (rng.standard_t(nu, size=(n_out, n_in)) * scale).astype(np.float32)
+    groups = w.reshape(n_out, n_in // group_size, group_size)
+    total = groups.shape[0] * groups.shape[1]
+    flat = groups.reshape(total, group_size)
+    n_const = int(round(const_frac * total))
+    n_zero = int(round(zero_frac * total))
+    pick = rng.choice(total, size=n_const + n_zero, replace=False)
+    flat[pick[:n_const]] = flat[pick[:n_const], :1]
+    flat[pick[n_const:]] = 0.0
+    return w
+
+
+def activations_f16(m, n_in, seed):
+    """fp16 [m][n_in] ~ N(0, 1) (drawn in float32, rounded to fp16 once)."""
+    return _rng(seed).standard_normal((m, n_in), dtype=np.float32).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# GPU-side generators for workloads too large to draw on the host.  They use
+# torch's seeded device generator; parity tests copy the rows they check back
+# to the host.
+# ---------------------------------------------------------------------------
+
+def normal_weight_device(n_out, n_in, seed, std, n_outlier_cols, device):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    w = torch.randn((n_out, n_in), generator=gen, device=device, dtype=torch.float32)
+    w.mul_(std)
+    cols = outlier_columns(n_in, n_outlier_cols, seed)
+    if cols.size:
+        idx = torch.from_numpy(cols).to(device)
+        w[:, idx] *= OUTLIER_SCALE
+    return w
+
+
+def activations_f16_device(m, n_in, seed, device):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.randn((m, n_in), generator=gen, device=device,
+                       dtype=torch.float32).half()
+
+
+# ---------------------------------------------------------------------------
+# Workload shapes.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Linear:
+    name: str
+    n_out: int
+    n_in: int
+
+
+# Llama-2-7B-shaped decoder layer: attention projections and the gated MLP.
+LLAMA7B_LINEARS = (
+    Linear("q", 4096, 4096), Linear("k", 4096, 4096), Linear("v", 4096, 4096),
+    Linear("o", 4096, 4096), Linear("gate", 11008, 4096), Linear("up", 11008, 4096),
+    Linear("down", 4096, 11008),
+)
+LLAMA7B_LAYERS = 32
+
+# 70B-shaped decoder layer (grouped-query attention: 8 KV heads of 128).
+LLAMA70B_LINEARS = (
+    Linear("q", 8192, 8192), Linear("k", 1024, 8192), Linear("v", 1024, 8192),
+    Linear("o", 8192, 8192), Linear("gate", 28672, 8192), Linear("up", 28672, 8192),
+    Linear("down", 8192, 28672),
+)
+LLAMA70B_LAYERS = 80
+
+# Prefill GEMM shapes (7B projections), M = 2048 tokens.
+PREFILL_M = 2048
+PREFILL_LINEARS = (Linear("qkvo", 4096, 4096), Linear("gate_up", 11008, 4096),
+                   Linear("down", 4096, 11008))
+
+
+def llama7b_seed(layer, index):
+    return 2000 + 16 * layer + index
+
+
+def llama70b_seed(layer, index):
+    return 3000 + 8 * layer + index
+
+
+def n_outliers(n_in):
+    """About 0.1 % of the input columns."""
+    return int(round(0.001 * n_in))
