@@ -1,0 +1,132 @@
+/*
+ * w4a16.h -- C ABI of the W4A16 library for AMD Instinct MI355X (gfx950):
+ * group-wise INT4 weight quantization with packing, dequantization, and the
+ * linear layer y = x W'^T that unpacks and dequantizes the weights on the fly
+ * (decode GEMV for 1..16 rows of x, prefill GEMM for any number of rows).
+ *
+ * Sources (cited by page title and section):
+ *   [Guide] "27届大模型面试准备十九 模型量化全攻略 -- INT8/INT4、GPTQ、AWQ、
+ *           SmoothQuant 与 KV Cache 量化" (dksg.cn)
+ *   [Path]  "从 FP32 到 INT4：大模型推理加速中的量化优化实战路径" (adg.csdn.net)
+ *   [Zero]  "从0到1：大模型量化" (pinyinjj.github.io)
+ *   [Kern]  "大模型量化技术定义与主流方案解析" (cloud.baidu.com)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are device pointers (memory from hipMalloc or a torch CUDA
+ *    tensor), owned by the caller.  The library never allocates, frees or
+ *    synchronizes.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and is complete only when the caller synchronizes it.
+ *  - Layouts are dense row-major.  W and W' are [n_out][n_in] ([Guide] §2.2
+ *    takes W as [out_features, in_features]); groups run along n_in.
+ *  - fp16 values travel as uint16_t bit patterns (IEEE binary16).
+ *  - Packed weights: uint32_t [n_out][n_in / 8]; element k of a row is the
+ *    4-bit code in bits 4*(k % 8) .. 4*(k % 8) + 3 of word k / 8.
+ *  - Scales and zero-points: fp16 [n_out][n_in / group_size].  Symmetric
+ *    quantization stores its signed codes q in [-8, 7] as q + 8 with a stored
+ *    zero-point of 8, so every consumer computes w' = s * (code - z).
+ *  - Outputs are fully overwritten; inputs must not overlap outputs.
+ *  - Return value: Q4_OK, or one of the Q4_ERR_* codes below.  Argument
+ *    errors are detected before any HIP call is made.  A fault inside a
+ *    kernel surfaces at the caller's next synchronization, not here.
+ *  - Supported group sizes are 32, 64, 128 and 256 ([Zero] §3.1 names
+ *    blocks of 32 and 256, [Path] §2.2 groups of 128 and 64).  Any other size
+ *    is rejected with Q4_ERR_GROUP rather than served by a slow generic path.
+ *  - Inputs containing NaN or Inf give unspecified (but memory-safe) results.
+ *  - Calls are thread-safe; the library keeps no mutable global state.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1
+
+enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,   /* a required pointer is NULL */
+    Q4_ERR_SHAPE = 2,  /* a size <= 0 or too large, n_in % group_size != 0,
+                          or m outside the entry point's range */
+    Q4_ERR_GROUP = 3,  /* group_size not in {32, 64, 128, 256} */
+    Q4_ERR_ALIGN = 4,  /* w, w_out, qweight or x not 16-byte aligned, or an
+                          fp16 array not 2-byte aligned */
+    Q4_ERR_HIP = 5     /* the HIP runtime refused the launch; see
+                          q4_last_hip_error() */
+};
+
+/* Largest sizes accepted: n_in <= 2^20, n_out <= 2^24, m <= 2^24, and
+ * n_out * n_in <= 2^36 elements. */
+
+/* Q4_ABI_VERSION of the loaded library. */
+int q4_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *q4_strerror(int status);
+
+/* hipError_t of the last launch failure on the calling thread (0 if none). */
+int q4_last_hip_error(void);
+
+/*
+ * Group-wise INT4 quantization and packing of W (fp32 [n_out][n_in]).
+ * For every group of `group_size` consecutive elements of a row, all in
+ * binary32 with round-to-nearest-even ([Guide] §2.1 gives the affine map
+ * q = clamp(round(x/s) + z) with min-max calibration; [Path] §2.1 clips z
+ * and the codes):
+ *   asymmetric: s = max((max - min) / 15, 1e-8), z = clamp(rint(-min/s), 0, 15),
+ *               code = clamp(rint(w/s) + z, 0, 15);
+ *   symmetric:  s = max(max|w| / 7, 1e-8), q = clamp(rint(w/s), -8, 7),
+ *               code = q + 8, stored zero-point 8.
+ * Writes qweight (u32 [n_out][n_in/8]), scales = fp16(s) and zeros = fp16(z)
+ * (fp16 [n_out][n_in/group_size]).  Results are bit-exact: every step is a
+ * single IEEE operation, independent of launch configuration.
+ * w and qweight must be 16-byte aligned.
+ */
+int q4_quantize_pack(const float *w, int64_t n_out, int64_t n_in,
+                     int32_t group_size, int32_t symmetric,
+                     uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                     void *stream);
+
+/*
+ * Dequantization w' = s * (code - z) into fp32 w_out [n_out][n_in]
+ * ([Guide] §2.1, dequantize_tensor; [Zero] §2, f' = S (q - Z)).  The product
+ * of an fp16 scale and an integer in [-15, 15] is exact in binary32, so the
+ * result is bit-exact.  qweight and w_out must be 16-byte aligned.
+ */
+int q4_dequant(const uint32_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+               int64_t n_out, int64_t n_in, int32_t group_size, float *w_out,
+               void *stream);
+
+/*
+ * Decode-shaped W4A16 linear layer: y = x W'^T for 1 <= m <= 16, with
+ * x fp16 [m][n_in] and y fp16 [m][n_out].  The packed weights are unpacked
+ * and dequantized in registers and never written back ([Kern] §4: fused
+ * dequantization inside the matrix product; [Guide] §2.3: INT4 weights, FP16
+ * activations).  Products accumulate in fp32; y is rounded to fp16 once.
+ * Error bound per element: |y - x w'| <= 2e-3 * sum_k |x_k w'_k| + 1e-5.
+ * Results are deterministic for a given shape.  qweight and x must be
+ * 16-byte aligned.  m > 16 returns Q4_ERR_SHAPE (use q4_gemm).
+ */
+int q4_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
+            int32_t group_size, uint16_t *y, void *stream);
+
+/*
+ * Prefill-shaped W4A16 linear layer: the same contract as q4_gemv for any
+ * m >= 1, organised for large m: packed weight tiles are dequantized into
+ * LDS as fp16 and fed to the fp16 matrix cores with fp32 accumulation
+ * ([Guide] §2.3: W4A16 dequantizes to FP16 before the product, so prefill is
+ * compute-bound).  Same error bound and alignment rules as q4_gemv.
+ */
+int q4_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
+            int32_t group_size, uint16_t *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,64 @@
+"""Builds libw4a16.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+    python -m w4a16_dequant_gemv_amd.build
+
+Every translation unit is compiled with packed-fp32 instruction selection
+disabled; the quantizer's unit additionally keeps each fp32 operation
+separate (no FMA contraction) and uses correctly rounded fp32 division, which
+its bit-exactness depends on.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libw4a16.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+PER_FILE = {
+    "q4_quantize.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+                        "-fno-fast-math"],
+}
+SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip"]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 target feature; that
+    # warning is expected and dropped here.
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    if err.strip():
+        print(err, file=sys.stderr)
+    return obj
+
+
+def build(verbose=True):
+    """Compile every source and link libw4a16.so; returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+                   check=True)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,123 @@
+// q4_api.hip -- the C ABI declared in include/w4a16.h: argument validation
+// (before any HIP call), then one launch on the caller's stream.
+#include "w4a16.h"
+
+#include "q4_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxIn = int64_t(1) << 20;
+constexpr int64_t kMaxOut = int64_t(1) << 24;
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+constexpr int64_t kMaxElems = int64_t(1) << 34;
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_group(int32_t group_size)
+{
+    switch (group_size) {
+    case 32: case 64: case 128: case 256: return Q4_OK;
+    default: return Q4_ERR_GROUP;
+    }
+}
+
+// Shape rules common to every entry point: positive sizes within limits and
+// whole groups per row (the n_in % 8 packing rule follows from g >= 32).
+int check_weight_shape(int64_t n_out, int64_t n_in, int32_t group_size)
+{
+    if (n_out <= 0 || n_in <= 0 || n_out > kMaxOut || n_in > kMaxIn) return Q4_ERR_SHAPE;
+    if (n_out * n_in > kMaxElems) return Q4_ERR_SHAPE;
+    if (int rc = check_group(group_size)) return rc;
+    if (n_in % group_size != 0) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+int finish(hipError_t e)
+{
+    if (e == hipSuccess) return Q4_OK;
+    g_last_hip_error = (int)e;
+    return Q4_ERR_HIP;
+}
+
+int check_linear(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                 const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
+                 int32_t group_size, const uint16_t *y, int64_t max_m)
+{
+    if (!x || !qweight || !scales || !zeros || !y) return Q4_ERR_NULL;
+    if (int rc = check_weight_shape(n_out, n_in, group_size)) return rc;
+    if (m <= 0 || m > max_m || m * n_in > kMaxElems || m * n_out > kMaxElems) return Q4_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 2) ||
+        !aligned(y, 2))
+        return Q4_ERR_ALIGN;
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_abi_version(void) { return Q4_ABI_VERSION; }
+
+const char *q4_strerror(int status)
+{
+    switch (status) {
+    case Q4_OK: return "success";
+    case Q4_ERR_NULL: return "a required pointer is NULL";
+    case Q4_ERR_SHAPE: return "invalid shape: a size is <= 0 or too large, n_in is not a multiple "
+                              "of group_size, or m is outside the entry point's range";
+    case Q4_ERR_GROUP: return "unsupported group_size (supported: 32, 64, 128, 256)";
+    case Q4_ERR_ALIGN: return "misaligned pointer: w, w_out, qweight and x need 16 bytes, fp16 "
+                              "arrays 2 bytes";
+    case Q4_ERR_HIP: return "the HIP runtime refused the launch (see q4_last_hip_error)";
+    default: return "unknown status";
+    }
+}
+
+int q4_last_hip_error(void) { return g_last_hip_error; }
+
+int q4_quantize_pack(const float *w, int64_t n_out, int64_t n_in, int32_t group_size,
+                     int32_t symmetric, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                     void *stream)
+{
+    if (!w || !qweight || !scales || !zeros) return Q4_ERR_NULL;
+    if (int rc = check_weight_shape(n_out, n_in, group_size)) return rc;
+    if (!aligned(w, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+        return Q4_ERR_ALIGN;
+    return finish(q4_launch_quantize_pack(w, n_out, n_in, group_size, symmetric != 0, qweight,
+                                          scales, zeros, (hipStream_t)stream));
+}
+
+int q4_dequant(const uint32_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+               int64_t n_out, int64_t n_in, int32_t group_size, float *w_out, void *stream)
+{
+    if (!qweight || !scales || !zeros || !w_out) return Q4_ERR_NULL;
+    if (int rc = check_weight_shape(n_out, n_in, group_size)) return rc;
+    if (!aligned(qweight, 16) || !aligned(w_out, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+        return Q4_ERR_ALIGN;
+    return finish(q4_launch_dequant(qweight, scales, zeros, n_out, n_in, group_size, w_out,
+                                    (hipStream_t)stream));
+}
+
+int q4_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in, int32_t group_size,
+            uint16_t *y, void *stream)
+{
+    if (int rc = check_linear(x, qweight, scales, zeros, m, n_out, n_in, group_size, y, 16))
+        return rc;
+    return finish(q4_launch_gemv(x, qweight, scales, zeros, m, n_out, n_in, group_size, y,
+                                 (hipStream_t)stream));
+}
+
+int q4_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in, int32_t group_size,
+            uint16_t *y, void *stream)
+{
+    if (int rc = check_linear(x, qweight, scales, zeros, m, n_out, n_in, group_size, y, kMaxRows))
+        return rc;
+    return finish(q4_launch_gemm(x, qweight, scales, zeros, m, n_out, n_in, group_size, y,
+                                 (hipStream_t)stream));
+}
+
+}  // extern "C"

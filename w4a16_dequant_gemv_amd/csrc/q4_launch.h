@@ -1,0 +1,21 @@
+// q4_launch.h -- internal launchers (validated arguments only; see q4_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+hipError_t q4_launch_quantize_pack(const float *w, int64_t n_out, int64_t n_in,
+                                   int group_size, bool symmetric, uint32_t *qweight,
+                                   uint16_t *scales, uint16_t *zeros, hipStream_t stream);
+
+hipError_t q4_launch_dequant(const uint32_t *qweight, const uint16_t *scales,
+                             const uint16_t *zeros, int64_t n_out, int64_t n_in,
+                             int group_size, float *out, hipStream_t stream);
+
+hipError_t q4_launch_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                          const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
+                          int group_size, uint16_t *y, hipStream_t stream);
+
+hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                          const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
+                          int group_size, uint16_t *y, hipStream_t stream);
