@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 hot path on one MI355X.
+
+Headline (`value`): decode GEMV throughput in HBM GB/s on a Llama-2-7B-shaped
+stack at m=1: 32 layers x 7 linears (q,k,v,o 4096x4096; gate,up 11008x4096;
+down 4096x11008), INT4 g=128 asymmetric, seeded synthetic weights
+N(0, 0.02) with 0.1 % outlier columns x50.  One step is one decode token
+through all 224 linears (3.45 GB of packed weights, far more than the 256 MB
+Infinity Cache), replayed from a captured HIP graph with every input already
+resident in HBM.  GB/s counts algorithmic bytes: packed codes (0.5 B/weight),
+fp16 scales and zero-points (4/g B/weight), x and y once per linear.
+
+Also measured in the same run and reported as extra keys:
+  prefill  -- q4_gemm at m=2048 on the three 7B projection shapes (TFLOP/s),
+  decode70b -- q4_gemv at m=8 over 80 layers of 70B-shaped linears (GB/s),
+  stress   -- q4_gemv at m=1 on 8192x28672 for g=128 and g=32 (GB/s),
+  quantize -- q4_quantize_pack and q4_dequant on 8192x28672 (GB/s),
+  cpu_baseline -- the CPU oracle (dequantize + binary64 product) timed on
+                  this host's cores on a bounded sample of the decode step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n_out, n_in, m, g):
+    """Bytes the method must move for one linear: codes, s and z, x and y."""
+    return n_out * n_in // 2 + 4 * n_out * (n_in // g) + 2 * m * n_in + 2 * m * n_out
+
+
+def time_graph(graph, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) * 1e-3, wall
+
+
+def capture(fn):
+    """Capture fn() (a sequence of library launches) into a CUDA/HIP graph."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                      # eager run on the capture stream first
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def gemv_sources_digest():
+    h = hashlib.sha256()
+    for f in ("q4_gemv.hip", "q4_device.h"):
+        with open(os.path.join(ROOT, "w4a16_dequant_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(bytes_per_launch):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current GEMV source; otherwise None."""
+    path = os.path.join(PROFILES, "gemv_llama7b_m1_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    m = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m or not t or m.group(1) != gemv_sources_digest():
+        return None
+    return float(t.group(1))
+
+
+# ---------------------------------------------------------------------------
+def build_decode_stack(layers, dev, keep_host_layer0):
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    xs = {k: syn.activations_f16_device(1, k, 2100 + k, dev) for k in (4096, 11008)}
+    linears, host_w = [], []
+    for layer in range(layers):
+        for i, lin in enumerate(syn.LLAMA7B_LINEARS):
+            w = syn.normal_weight_device(lin.n_out, lin.n_in, syn.llama7b_seed(layer, i), 0.02,
+                                         syn.n_outliers(lin.n_in), dev)
+            qw = w4.quantize_pack(w, 128)
+            if layer == 0 and keep_host_layer0:
+                host_w.append((lin, w.cpu().numpy()))
+            del w
+            y = torch.empty((1, lin.n_out), dtype=torch.float16, device=dev)
+            linears.append((lin, qw, xs[lin.n_in], y))
+    torch.cuda.synchronize()
+    return linears, host_w
+
+
+def bench_decode(args, dev):
+    import w4a16_dequant_gemv_amd as w4
+    layers = 32
+    t0 = time.perf_counter()
+    linears, host_w = build_decode_stack(layers, dev, keep_host_layer0=not args.no_cpu_baseline)
+    log(f"decode stack: {layers} layers x 7 linears quantized in {time.perf_counter() - t0:.1f} s")
+
+    def step():
+        for lin, qw, x, y in linears:
+            w4.gemv(x, qw, y)
+
+    graph = capture(step)
+    step_bytes = sum(algorithmic_bytes(l.n_out, l.n_in, 1, 128) for l, *_ in linears)
+    elapsed, wall = time_graph(graph, args.steps, args.warmup)
+    launches = len(linears)
+    per_launch_s = elapsed / (args.steps * launches)
+    res = dict(step_bytes=step_bytes, launches=launches, elapsed=elapsed, wall=wall,
+               ms_per_step=elapsed / args.steps * 1e3,
+               gbs=step_bytes * args.steps / elapsed / 1e9,
+               per_launch_us=per_launch_s * 1e6,
+               bytes_per_launch=step_bytes / launches)
+    return res, host_w
+
+
+def cpu_baseline(host_w, budget_s):
+    """Oracle GEMV (dequantize, then binary64 product) on layer 0's linears,
+    repeated until about `budget_s` seconds of CPU work."""
+    import numpy as np
+    import oracle
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    orc = oracle.load()
+    xs = {}
+    prepared = []
+    for lin, w in host_w:
+        packed, scales, zeros, _ = orc.quantize_pack(w, 128)      # untimed preparation
+        if lin.n_in not in xs:
+            xs[lin.n_in] = syn.activations_f16(1, lin.n_in, seed=2100 + lin.n_in).view(np.uint16)
+        prepared.append((lin, packed, scales, zeros))
+    done_bytes, t_cpu, n_lin = 0, 0.0, 0
+    while t_cpu < budget_s:
+        for lin, packed, scales, zeros in prepared:
+            t0 = time.perf_counter()
+            orc.linear_from_packed(xs[lin.n_in], packed, scales, zeros, 128)
+            t_cpu += time.perf_counter() - t0
+            done_bytes += algorithmic_bytes(lin.n_out, lin.n_in, 1, 128)
+            n_lin += 1
+            if t_cpu >= budget_s:
+                break
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return dict(value=round(done_bytes / t_cpu / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
+                sample=(f"{n_lin} decode linears (7B layer-0 shapes, m=1, g=128) through the C "
+                        f"oracle's dequantize + binary64 product, {t_cpu:.1f} s of CPU time"))
+
+
+def bench_prefill(args, dev):
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    out, tot_flop, tot_t = [], 0, 0.0
+    for i, lin in enumerate(syn.PREFILL_LINEARS):
+        w = syn.normal_weight_device(lin.n_out, lin.n_in, 4000 + i, 0.02, syn.n_outliers(lin.n_in), dev)
+        qw = w4.quantize_pack(w, 128)
+        del w
+        x = syn.activations_f16_device(syn.PREFILL_M, lin.n_in, 4100 + i, dev)
+        y = torch.empty((syn.PREFILL_M, lin.n_out), dtype=torch.float16, device=dev)
+        reps = 20
+        g = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
+        el, _ = time_graph(g, 3, 1)
+        t = el / (3 * reps)
+        flop = 2 * syn.PREFILL_M * lin.n_out * lin.n_in
+        out.append(dict(shape=f"{syn.PREFILL_M}x{lin.n_out}x{lin.n_in}", us=round(t * 1e6, 2),
+                        tflops=round(flop / t / 1e12, 1)))
+        tot_flop += flop
+        tot_t += t
+    return dict(shapes=out, tflops=round(tot_flop / tot_t / 1e12, 1))
+
+
+def bench_decode70b(args, dev):
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    layers = syn.LLAMA70B_LAYERS if not args.quick else 8
+    xs = {k: syn.activations_f16_device(8, k, 3100 + k, dev) for k in (8192, 28672)}
+    linears = []
+    t0 = time.perf_counter()
+    for layer in range(layers):
+        for i, lin in enumerate(syn.LLAMA70B_LINEARS):
+            w = syn.normal_weight_device(lin.n_out, lin.n_in, syn.llama70b_seed(layer, i), 0.015, 0, dev)
+            qw = w4.quantize_pack(w, 128)
+            del w
+            linears.append((lin, qw, xs[lin.n_in],
+                            torch.empty((8, lin.n_out), dtype=torch.float16, device=dev)))
+    torch.cuda.synchronize()
+    log(f"70B stack: {layers} layers quantized in {time.perf_counter() - t0:.1f} s")
+    g = capture(lambda: [w4.gemv(x, qw, y) for _, qw, x, y in linears])
+    el, _ = time_graph(g, 5, 1)
+    nbytes = sum(algorithmic_bytes(l.n_out, l.n_in, 8, 128) for l, *_ in linears)
+    res = dict(layers=layers, m=8, ms_per_pass=round(el / 5 * 1e3, 3),
+               gbs=round(nbytes * 5 / el / 1e9, 1), resident_gb=round(nbytes / 1e9, 2))
+    del linears, g
+    torch.cuda.empty_cache()
+    return res
+
+
+def student_t_device(n_out, n_in, seed, dev):
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    z = torch.randn((n_out, n_in), generator=gen, device=dev)
+    chi2 = torch.zeros_like(z)
+    for _ in range(3):
+        chi2.addcmul_(e := torch.randn((n_out, n_in), generator=gen, device=dev), e)
+    return z.mul_(torch.rsqrt(chi2.div_(3.0))).mul_(0.02)
+
+
+def bench_stress_and_quantize(args, dev):
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    n_out, n_in = 8192, 28672
+    w = student_t_device(n_out, n_in, 5, dev)
+    x = syn.activations_f16_device(1, n_in, 5100, dev)
+    res = {}
+    for g in (128, 32):
+        qws = [w4.quantize_pack(w, g)]
+        for c in range(1, 3):          # three copies (3 x 125-147 MB) to defeat the cache
+            qws.append(w4.quantize_pack(w.mul(1.0 + c * 1e-3), g))
+        y = torch.empty((1, n_out), dtype=torch.float16, device=dev)
+        reps = 8
+        gr = capture(lambda: [w4.gemv(x, qws[r % 3], y) for r in range(reps * 3)])
+        el, _ = time_graph(gr, 3, 1)
+        t = el / (3 * reps * 3)
+        res[f"gemv_g{g}_gbs"] = round(algorithmic_bytes(n_out, n_in, 1, g) / t / 1e9, 1)
+        res[f"gemv_g{g}_us"] = round(t * 1e6, 2)
+        del qws, gr
+    qw = w4.quantize_pack(w, 128)
+    out = torch.empty_like(w)
+    gq = capture(lambda: [w4.quantize_pack(w, 128, out=qw) for _ in range(5)])
+    el, _ = time_graph(gq, 2, 1)
+    qbytes = n_out * n_in * 4 + n_out * n_in // 2 + n_out * (n_in // 128) * 4
+    res["quantize_g128_gbs"] = round(qbytes * 10 / el / 1e9, 1)
+    gd = capture(lambda: [w4.dequant(qw, out) for _ in range(5)])
+    el, _ = time_graph(gd, 2, 1)
+    res["dequant_g128_gbs"] = round(qbytes * 10 / el / 1e9, 1)
+    del w, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="decode phase plus a short 70B stack")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the headline decode phase")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (the library has no CPU path)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+
+    decode, host_w = bench_decode(args, dev)
+    log(f"decode: {decode['gbs']:.1f} GB/s, {decode['ms_per_step']:.3f} ms/step, "
+        f"{decode['per_launch_us']:.2f} us per GEMV launch")
+    extras = {}
+    if not args.no_extras:
+        extras["prefill"] = bench_prefill(args, dev)
+        log(f"prefill: {extras['prefill']}")
+        extras["decode70b"] = bench_decode70b(args, dev)
+        log(f"decode70b: {extras['decode70b']}")
+        extras["stress"] = bench_stress_and_quantize(args, dev)
+        log(f"stress: {extras['stress']}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host_w, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+
+    achieved = decode["bytes_per_launch"] / (decode["per_launch_us"] * 1e-6) / 1e9
+    traffic = counters_traffic(decode["bytes_per_launch"])
+    record = {
+        "metric": "W4A16 decode GEMV HBM GB/s (% peak) + prefill GEMM TFLOPS (% MFMA peak)",
+        "value": round(decode["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(decode["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights with 0.1% outlier columns x50, x ~ N(0,1) fp16)",
+        "config": {"workload": "Llama-2-7B-shaped decode, m=1: 32 layers x 7 linears "
+                               "(4x 4096x4096, 2x 11008x4096, 4096x11008), INT4 g=128 asymmetric",
+                   "m": 1, "group_size": 128, "layers": 32, "linears_per_step": decode["launches"],
+                   "bytes_per_step": decode["step_bytes"], "launch": "HIP graph replay"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "q4_gemv (gemv_kernel)", "avg_launch_us": round(decode["per_launch_us"], 3),
+                     "bytes_per_launch": round(decode["bytes_per_launch"])},
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(decode["wall"], 4),
+    }
+    if "prefill" in extras:
+        tf = extras["prefill"]["tflops"]
+        record["prefill"] = dict(extras["prefill"], roofline={
+            "bound": "mfma", "achieved": tf, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+        record["decode70b"] = dict(extras["decode70b"], frac=round(extras["decode70b"]["gbs"] / HBM_PEAK_GBS, 4))
+        record["stress"] = extras["stress"]
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()
