@@ -101,77 +101,99 @@ def counters_traffic(bytes_per_launch):
 
 # ---------------------------------------------------------------------------
 def build_decode_stack(layers, dev, keep_host_layer0):
+    """Quantized 7B-shaped layers stored the way serving engines store them:
+    q, k, v concatenated into one [12288, 4096] matrix and gate, up into one
+    [22016, 4096] matrix (quantization is per row, so this equals quantizing
+    each linear alone).  Each of the four GEMVs of a layer has its own x."""
     import torch
     import w4a16_dequant_gemv_amd as w4
     from w4a16_dequant_gemv_amd import synthetic as syn
-    xs = {k: syn.activations_f16_device(1, k, 2100 + k, dev) for k in (4096, 11008)}
-    linears, host_w = [], []
+    lin = syn.LLAMA7B_LINEARS
+    fused = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+    xs = {name: syn.activations_f16_device(1, lin[idx[0]].n_in, 2100 + j, dev)
+          for j, (name, idx) in enumerate(fused)}
+    gemvs, host_w = [], []
     for layer in range(layers):
-        for i, lin in enumerate(syn.LLAMA7B_LINEARS):
-            w = syn.normal_weight_device(lin.n_out, lin.n_in, syn.llama7b_seed(layer, i), 0.02,
-                                         syn.n_outliers(lin.n_in), dev)
+        for name, idx in fused:
+            w = torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama7b_seed(layer, i),
+                                                    0.02, syn.n_outliers(lin[i].n_in), dev) for i in idx])
             qw = w4.quantize_pack(w, 128)
             if layer == 0 and keep_host_layer0:
-                host_w.append((lin, w.cpu().numpy()))
+                host_w.append((name, w.cpu().numpy(), xs[name].cpu().numpy()))
             del w
-            y = torch.empty((1, lin.n_out), dtype=torch.float16, device=dev)
-            linears.append((lin, qw, xs[lin.n_in], y))
+            y = torch.empty((1, qw.n_out), dtype=torch.float16, device=dev)
+            gemvs.append((name, qw, xs[name], y))
     torch.cuda.synchronize()
-    return linears, host_w
+    return gemvs, host_w
 
 
 def bench_decode(args, dev):
     import w4a16_dequant_gemv_amd as w4
     layers = 32
     t0 = time.perf_counter()
-    linears, host_w = build_decode_stack(layers, dev, keep_host_layer0=not args.no_cpu_baseline)
+    gemvs, host_w = build_decode_stack(layers, dev, keep_host_layer0=not args.no_cpu_baseline)
     log(f"decode stack: {layers} layers x 7 linears quantized in {time.perf_counter() - t0:.1f} s")
 
     def step():
-        for lin, qw, x, y in linears:
+        for _, qw, x, y in gemvs:
             w4.gemv(x, qw, y)
 
     graph = capture(step)
-    step_bytes = sum(algorithmic_bytes(l.n_out, l.n_in, 1, 128) for l, *_ in linears)
+    step_bytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 1, 128) for _, qw, _, _ in gemvs)
     elapsed, wall = time_graph(graph, args.steps, args.warmup)
-    launches = len(linears)
+    launches = len(gemvs)
     per_launch_s = elapsed / (args.steps * launches)
     res = dict(step_bytes=step_bytes, launches=launches, elapsed=elapsed, wall=wall,
                ms_per_step=elapsed / args.steps * 1e3,
                gbs=step_bytes * args.steps / elapsed / 1e9,
                per_launch_us=per_launch_s * 1e6,
                bytes_per_launch=step_bytes / launches)
+    # The same weights with one launch per linear (7 per layer): row slices
+    # of the fused matrices are themselves valid packed weights.
+    from w4a16_dequant_gemv_amd.api import QuantizedWeight
+    split = {"qkv": (4096, 4096, 4096), "gate_up": (11008, 11008)}
+    per_linear = []
+    for name, qw, x, y in gemvs:
+        off = 0
+        for n in split.get(name, (qw.n_out,)):
+            sl = slice(off, off + n)
+            per_linear.append((QuantizedWeight(qw.qweight[sl], qw.scales[sl], qw.zeros[sl], n, qw.n_in, 128),
+                               x, y[:, sl]))
+            off += n
+    res["gbs_7_launches_per_layer"] = None
+    if not args.decode_only:
+        graph7 = capture(lambda: [w4.gemv(x, q, y) for q, x, y in per_linear])
+        el7, _ = time_graph(graph7, max(1, args.steps // 2), 1)
+        res["gbs_7_launches_per_layer"] = round(step_bytes * max(1, args.steps // 2) / el7 / 1e9, 1)
+        del graph7
     return res, host_w
 
 
 def cpu_baseline(host_w, budget_s):
-    """Oracle GEMV (dequantize, then binary64 product) on layer 0's linears,
-    repeated until about `budget_s` seconds of CPU work."""
+    """Oracle GEMV (dequantize, then binary64 product) on layer 0's four
+    fused linears, repeated until about `budget_s` seconds of CPU work."""
     import numpy as np
     import oracle
-    from w4a16_dequant_gemv_amd import synthetic as syn
     orc = oracle.load()
-    xs = {}
     prepared = []
-    for lin, w in host_w:
+    for name, w, x in host_w:
         packed, scales, zeros, _ = orc.quantize_pack(w, 128)      # untimed preparation
-        if lin.n_in not in xs:
-            xs[lin.n_in] = syn.activations_f16(1, lin.n_in, seed=2100 + lin.n_in).view(np.uint16)
-        prepared.append((lin, packed, scales, zeros))
+        prepared.append((name, packed, scales, zeros, x.view(np.uint16)))
     done_bytes, t_cpu, n_lin = 0, 0.0, 0
     while t_cpu < budget_s:
-        for lin, packed, scales, zeros in prepared:
+        for name, packed, scales, zeros, x in prepared:
             t0 = time.perf_counter()
-            orc.linear_from_packed(xs[lin.n_in], packed, scales, zeros, 128)
+            orc.linear_from_packed(x, packed, scales, zeros, 128)
             t_cpu += time.perf_counter() - t0
-            done_bytes += algorithmic_bytes(lin.n_out, lin.n_in, 1, 128)
+            done_bytes += algorithmic_bytes(packed.shape[0], packed.shape[1] * 8, 1, 128)
             n_lin += 1
             if t_cpu >= budget_s:
                 break
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
     return dict(value=round(done_bytes / t_cpu / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
-                sample=(f"{n_lin} decode linears (7B layer-0 shapes, m=1, g=128) through the C "
-                        f"oracle's dequantize + binary64 product, {t_cpu:.1f} s of CPU time"))
+                sample=(f"{n_lin} fused decode GEMVs of the 7B layer-0 shapes (qkv 12288x4096, o 4096x4096, "
+                        f"gate_up 22016x4096, down 4096x11008; m=1, g=128) through the C oracle's "
+                        f"dequantize + binary64 product, {t_cpu:.1f} s of CPU time"))
 
 
 def bench_prefill(args, dev):
@@ -198,28 +220,33 @@ def bench_prefill(args, dev):
 
 
 def bench_decode70b(args, dev):
+    """80 layers of 70B-shaped linears at m=8, stored fused like the 7B stack:
+    qkv [10240, 8192], o [8192, 8192], gate_up [57344, 8192], down [8192, 28672]."""
     import torch
     import w4a16_dequant_gemv_amd as w4
     from w4a16_dequant_gemv_amd import synthetic as syn
     layers = syn.LLAMA70B_LAYERS if not args.quick else 8
-    xs = {k: syn.activations_f16_device(8, k, 3100 + k, dev) for k in (8192, 28672)}
-    linears = []
+    lin = syn.LLAMA70B_LINEARS
+    fused = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+    xs = {name: syn.activations_f16_device(8, lin[idx[0]].n_in, 3100 + j, dev)
+          for j, (name, idx) in enumerate(fused)}
+    gemvs = []
     t0 = time.perf_counter()
     for layer in range(layers):
-        for i, lin in enumerate(syn.LLAMA70B_LINEARS):
-            w = syn.normal_weight_device(lin.n_out, lin.n_in, syn.llama70b_seed(layer, i), 0.015, 0, dev)
+        for name, idx in fused:
+            w = torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama70b_seed(layer, i),
+                                                    0.015, 0, dev) for i in idx])
             qw = w4.quantize_pack(w, 128)
             del w
-            linears.append((lin, qw, xs[lin.n_in],
-                            torch.empty((8, lin.n_out), dtype=torch.float16, device=dev)))
+            gemvs.append((qw, xs[name], torch.empty((8, qw.n_out), dtype=torch.float16, device=dev)))
     torch.cuda.synchronize()
     log(f"70B stack: {layers} layers quantized in {time.perf_counter() - t0:.1f} s")
-    g = capture(lambda: [w4.gemv(x, qw, y) for _, qw, x, y in linears])
+    g = capture(lambda: [w4.gemv(x, qw, y) for qw, x, y in gemvs])
     el, _ = time_graph(g, 5, 1)
-    nbytes = sum(algorithmic_bytes(l.n_out, l.n_in, 8, 128) for l, *_ in linears)
-    res = dict(layers=layers, m=8, ms_per_pass=round(el / 5 * 1e3, 3),
+    nbytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 8, 128) for qw, _, _ in gemvs)
+    res = dict(layers=layers, m=8, gemvs_per_pass=len(gemvs), ms_per_pass=round(el / 5 * 1e3, 3),
                gbs=round(nbytes * 5 / el / 1e9, 1), resident_gb=round(nbytes / 1e9, 2))
-    del linears, g
+    del gemvs, g
     torch.cuda.empty_cache()
     return res
 
@@ -277,6 +304,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="decode phase plus a short 70B stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline decode phase")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the timed decode graph (no extras, no per-linear reference, no CPU leg); "
+                         "used for profiling")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
 
@@ -291,6 +321,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
 
+    if args.decode_only:
+        args.no_extras = True
+        args.no_cpu_baseline = True
     decode, host_w = bench_decode(args, dev)
     log(f"decode: {decode['gbs']:.1f} GB/s, {decode['ms_per_step']:.3f} ms/step, "
         f"{decode['per_launch_us']:.2f} us per GEMV launch")
@@ -323,9 +356,10 @@ def main():
         "dtype": "int4 weights x fp16 activations, fp32 accumulate",
         "data": "synthetic (seeded N(0,0.02) weights with 0.1% outlier columns x50, x ~ N(0,1) fp16)",
         "config": {"workload": "Llama-2-7B-shaped decode, m=1: 32 layers x 7 linears "
-                               "(4x 4096x4096, 2x 11008x4096, 4096x11008), INT4 g=128 asymmetric",
-                   "m": 1, "group_size": 128, "layers": 32, "linears_per_step": decode["launches"],
-                   "bytes_per_step": decode["step_bytes"], "launch": "HIP graph replay"},
+                               "(q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008), INT4 g=128 asymmetric",
+                   "m": 1, "group_size": 128, "layers": 32, "gemvs_per_step": decode["launches"],
+                   "bytes_per_step": decode["step_bytes"],
+                   "launch": "HIP graph replay; per layer 4 dependent GEMVs: fused qkv, o, fused gate_up, down"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
@@ -333,6 +367,7 @@ def main():
                      "bytes_per_launch": round(decode["bytes_per_launch"])},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(decode["wall"], 4),
+        "decode_7_launches_per_layer_gbs": decode["gbs_7_launches_per_layer"],
     }
     if "prefill" in extras:
         tf = extras["prefill"]["tflops"]

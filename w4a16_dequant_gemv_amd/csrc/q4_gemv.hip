@@ -6,14 +6,12 @@
 // weight byte is read once per call and the arithmetic intensity is a few
 // FLOP per byte, so the kernel is bound by HBM bandwidth.
 //
-// What limits it on gfx950 is the number of vector-memory instructions, not
-// arithmetic: every global load, however small, occupies the CU's address
-// and data path for several cycles, so per-lane gathers of x, scales and
-// zero-points cost as much as the 1-KiB weight loads themselves.  The kernel
-// therefore issues exactly one global load per 1 KiB of packed weights per
-// wave; x (pre-permuted into MFMA fragment order) and the scale|zero pairs
-// of the workgroup's rows are staged cooperatively in LDS, one k window at a
-// time, and read back with ds_read.
+// What limits it on gfx950 is how many weight bytes each CU keeps in flight,
+// not arithmetic.  Per-lane gathers of x, scales and zero-points cost as many
+// vector-memory issue slots as the 1-KiB weight loads themselves, so x
+// (pre-permuted into MFMA fragment order) and the scale|zero pairs of the
+// workgroup's rows are staged cooperatively in LDS and read back with
+// ds_read, and each wave issues one global load per 1 KiB of weights.
 //
 // Matrix-core mapping.  v_mfma_f32_16x16x32_f16 multiplies a 16x32 A block
 // (rows = the m rows of x, padded to 16 with copies of row m-1 whose results
@@ -44,269 +42,135 @@
 //    and multiplying by s in fp16 (the only rounding, 2^-11 relative).
 //
 // Work split.  A workgroup of SPLIT waves owns CT tiles of 16 output
-// channels.  k is cut into windows of WB = SPLIT * UNROLL blocks; in each
-// window wave w handles blocks w*UNROLL .. w*UNROLL + UNROLL - 1, so the
-// workgroup reads WB * 64 contiguous bytes of each of its rows per window.
-// The next window's weights (registers) and x / scale|zero (registers, then
-// LDS) are fetched while the current window is computed; one barrier per
-// window hands the LDS buffers over.  Partial results of the SPLIT waves are
-// summed in LDS in a fixed order, so results are deterministic.
+// channels.  Its k blocks are dealt out in stages of SPLIT * UNROLL: in stage
+// i wave w takes blocks (i * SPLIT + w) * UNROLL + u, so at any moment the
+// workgroup reads a contiguous run of each of its rows.  Two kernels:
+//  * resident: all of x and all scale|zero pairs of the workgroup's rows fit
+//    in LDS (gfx950 gives a workgroup up to 160 KiB).  They are staged once,
+//    behind a single barrier, and every wave then streams its weights through
+//    a ring of DEPTH register stages with no further synchronization.
+//  * windowed: for larger m * n_in, x and scale|zero pairs are staged one
+//    window (one stage of blocks) ahead in double-buffered LDS, with one
+//    barrier per window.
+// Loads past the last block are redirected to x (hot in L2) rather than
+// re-reading weights, so no load is conditional and the compiler keeps the
+// ring in flight.  Partial results of the SPLIT waves are summed in LDS in a
+// fixed order, so results are deterministic.
 #include "q4_device.h"
 #include "q4_launch.h"
 
 namespace {
-
-// Per-lane weight registers for one window: UNROLL blocks x CT tiles.
-template <int CT, int UNROLL>
-struct Stage {
-    u32x4 w[UNROLL][CT];
-};
-
-// Cooperative copy of one window's x and scale|zero pairs: each thread owns
-// at most XC chunks of 32 x values and SC (row, group) items.
-template <int XC, int SC>
-struct Coop {
-    u32x4 x[XC][4];
-    uint16_t s[SC], z[SC];
-};
-
-// Eight consecutive x values (four dwords) -> the dwords (x[t], x[t+4]) of
-// MFMA t, for the j-th word of a lane's 32 codes.
-__device__ __forceinline__ uint32_t pick_pair(const u32x4 &v, int t)
-{
-    const uint32_t lo = v[t >> 1], hi = v[(t >> 1) + 2];
-    return __builtin_amdgcn_perm(hi, lo, (t & 1) ? 0x07060302u : 0x05040100u);
-}
 
 struct Geometry {
     int m, n_out, n_in, group_shift;
     int words_per_row, groups_per_row, kblocks;
     int last_full_quarter;  // quarters beyond it in the last block are padding
     int sz_stride;          // u32 per LDS row of scale|zero pairs (odd)
-    int x_row_bytes;        // LDS bytes per x row per window (padded)
+    int x_row_bytes;        // LDS bytes per row of x (padded)
+    int sz_vector;          // scale/zero arrays allow 16-byte loads
 };
 
-template <int SPLIT, int CT, int UNROLL, bool FOLD>
-__global__ __launch_bounds__(64 * SPLIT) void gemv_kernel(
-    const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    uint16_t *__restrict__ y, Geometry geo)
+// Per-lane weight registers of one stage: UNROLL blocks x CT tiles.
+template <int CT, int UNROLL>
+struct Stage {
+    u32x4 w[UNROLL][CT];
+};
+
+// Eight consecutive x values (four dwords) -> the dword (x[t], x[t+4]) used
+// by MFMA t.
+__device__ __forceinline__ uint32_t pick_pair(const u32x4 &v, int t)
 {
-    constexpr int THREADS = 64 * SPLIT;
-    constexpr int WB = SPLIT * UNROLL;          // k blocks per window
-    constexpr int ROWS = 16 * CT;               // output channels per workgroup
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const uint32_t lo = v[t >> 1], hi = v[(t >> 1) + 2];
+    return __builtin_amdgcn_perm(hi, lo, (t & 1) ? 0x07060302u : 0x05040100u);
+}
 
-    const int m = geo.m, n_out = geo.n_out, n_in = geo.n_in, gshift = geo.group_shift;
-    const int kblocks = geo.kblocks;
-    const int groups_win = (WB * 128) >> gshift;        // groups per row per window
-    const int x_buf_bytes = m * geo.x_row_bytes;
-    const int sz_buf_bytes = ROWS * geo.sz_stride * 4;
-    char *x_lds = lds;                                   // [2][m][x_row_bytes]
-    char *sz_lds = lds + 2 * x_buf_bytes;                // [2][ROWS][sz_stride] u32
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 15;
-    const int quarter = lane >> 4;
-    const int row0 = blockIdx.x * ROWS;
-    const int nwin = (kblocks + WB - 1) / WB;
-
-    // ---- per-lane weight addressing (wave-uniform base + fixed offset) ----
-    const char *qbase = reinterpret_cast<const char *>(qweight + (int64_t)row0 * geo.words_per_row);
-    uint32_t woff[CT];
+// LDS layout of x: per row, per block of 128 k: [t][quarter] x 16 bytes, i.e.
+// the A fragment of MFMA t for lane quarter q sits at kb*256 + t*64 + q*16.
+// Four consecutive 16-byte x chunks (32 values at k = 32q ..) -> their four
+// fragment dwords-quads, written at t*64 + q*16 (conflict-free: consecutive
+// chunks land in consecutive 16-byte slots).
+__device__ __forceinline__ void store_x_chunk(char *row_block, int quarter, const u32x4 c[4])
+{
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
-        const int r = min(t * 16 + col, n_out - 1 - row0);
-        woff[t] = (uint32_t)(r * geo.words_per_row + quarter * 4) * 4u;
+    for (int t = 0; t < 4; ++t) {
+        u32x4 d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = pick_pair(c[j], t);
+        *reinterpret_cast<u32x4 *>(row_block + t * 64 + quarter * 16) = d;
     }
-    auto qshift_of = [&](int kb) {
-        return (kb == kblocks - 1 && quarter > geo.last_full_quarter) ? geo.last_full_quarter - quarter : 0;
-    };
-    auto load_weights = [&](Stage<CT, UNROLL> &st, int win) {
+}
+
+// One 128-wide k block of CT tiles: B from the packed words, A from LDS,
+// scale|zero from LDS; `valid` false contributes nothing.
+template <int CT, bool FOLD>
+__device__ __forceinline__ void process_block(f32x4 acc[CT], const f16x8 a[4], const u32x4 w[CT],
+                                              const uint32_t sz[CT], bool valid)
+{
+    if (FOLD) {
+        // X = 2^-24 * sum of this lane-row's x over the block.
+        const f16x8 tiny = bitcast<f16x8>(u32x4{0x00010001u, 0x00010001u, 0x00010001u, 0x00010001u});
+        f32x4 xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], tiny, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int kb = min(win * WB + wave * UNROLL + u, kblocks - 1);
-            // a masked quarter is moved back onto the last whole slice; the
-            // offset is summed as a 32-bit value before it meets the base
-            const uint32_t kw = (uint32_t)(kb * 16 + qshift_of(kb) * 4) * 4u;
+        for (int t = 1; t < 4; ++t) xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], tiny, xs, 0, 0, 0);
 #pragma unroll
-            for (int t = 0; t < CT; ++t) {
-                const uint32_t wo = woff[t] + kw;
-                st.w[u][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qbase + wo));
+        for (int c = 0; c < CT; ++c) {
+            u32x4 b0, b1, b2, b3;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t v = w[c][j];
+                const uint32_t v8 = v >> 8;
+                b0[j] = v & 0x000F000Fu;     // codes 0,4 as c * 2^-24
+                b1[j] = v & 0x00F000F0u;     // codes 1,5 as c * 2^-20
+                b2[j] = v8 & 0x000F000Fu;    // codes 2,6 as c * 2^-24
+                b3[j] = v8 & 0x00F000F0u;    // codes 3,7 as c * 2^-20
+            }
+            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 p24 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], bitcast<f16x8>(b0), zero4, 0, 0, 0);
+            f32x4 p20 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], bitcast<f16x8>(b1), zero4, 0, 0, 0);
+            p24 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], bitcast<f16x8>(b2), p24, 0, 0, 0);
+            p20 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], bitcast<f16x8>(b3), p20, 0, 0, 0);
+            const float s = valid ? half_bits_to_float((uint16_t)sz[c]) * 16777216.0f : 0.0f;  // s * 2^24, exact
+            const float nz = -half_bits_to_float((uint16_t)(sz[c] >> 16));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = __builtin_fmaf(p20[r], 0.0625f, p24[r]);
+                acc[c][r] = __builtin_fmaf(s, __builtin_fmaf(nz, xs[r], v), acc[c][r]);
             }
         }
-    };
-
-    // ---- cooperative staging of x and scale|zero pairs for one window ----
-    constexpr int MAX_XCHUNKS = 16 * WB * 4;               // m <= 16 rows
-    constexpr int XC = (MAX_XCHUNKS + THREADS - 1) / THREADS;
-    constexpr int MAX_SITEMS = ROWS * WB * 4;              // group_size >= 32
-    constexpr int SC = (MAX_SITEMS + THREADS - 1) / THREADS;
-    const int n_xchunks = m * WB * 4;
-    const int n_sitems = ROWS * groups_win;
-    auto coop_load = [&](Coop<XC, SC> &c, int win) {
+    } else {
 #pragma unroll
-        for (int i = 0; i < XC; ++i) {
-            const int ch = tid + i * THREADS;
-            const int cc = min(ch, n_xchunks - 1);          // idle threads repeat a valid chunk
-            const int r = cc / (WB * 4), rem = cc % (WB * 4);
-            const int kb = min(win * WB + rem / 4, kblocks - 1);
-            const int k = min((kb << 7) + ((rem & 3) << 5), n_in - 32);
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (int64_t)r * n_in + k);
+        for (int c = 0; c < CT; ++c) {
+            const _Float16 s = valid ? bitcast<_Float16>((uint16_t)sz[c]) : (_Float16)0.0f;
+            const _Float16 zb = bitcast<_Float16>((uint16_t)(sz[c] >> 16)) + (_Float16)1024.0f;
+            const f16x2 scale = {s, s}, bias = {zb, zb};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) c.x[i][j] = src[j];
-        }
+            for (int p = 0; p < 4; ++p) {
+                u32x4 b;
 #pragma unroll
-        for (int i = 0; i < SC; ++i) {
-            const int it = min(tid + i * THREADS, n_sitems - 1);
-            const int r = min(row0 + it / groups_win, n_out - 1);
-            const int gidx = min(win * groups_win + it % groups_win, geo.groups_per_row - 1);
-            const int64_t off = (int64_t)r * geo.groups_per_row + gidx;
-            c.s[i] = scales[off];
-            c.z[i] = zeros[off];
-        }
-    };
-    auto coop_store = [&](const Coop<XC, SC> &c, int buf) {
-#pragma unroll
-        for (int i = 0; i < XC; ++i) {
-            const int ch = tid + i * THREADS;
-            if (ch < n_xchunks) {
-                const int r = ch / (WB * 4), rem = ch % (WB * 4);     // rem = block * 4 + quarter
-                char *dst = x_lds + buf * x_buf_bytes + r * geo.x_row_bytes + rem * 64;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    u32x4 d;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) d[j] = pick_pair(c.x[i][j], t);
-                    *reinterpret_cast<u32x4 *>(dst + 16 * t) = d;
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t h = ((w[c][j] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
+                    b[j] = bitcast<uint32_t>((bitcast<f16x2>(h) - bias) * scale);
                 }
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p], bitcast<f16x8>(b), acc[c], 0, 0, 0);
             }
         }
-#pragma unroll
-        for (int i = 0; i < SC; ++i) {
-            const int it = tid + i * THREADS;
-            if (it < n_sitems) {
-                const int r = it / groups_win, gw = it % groups_win;
-                reinterpret_cast<uint32_t *>(sz_lds + buf * sz_buf_bytes)[r * geo.sz_stride + gw] =
-                    (uint32_t)c.s[i] | ((uint32_t)c.z[i] << 16);
-            }
-        }
-    };
-
-    f32x4 acc[CT];
-#pragma unroll
-    for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int xrow = min(col, m - 1);
-    auto compute = [&](const Stage<CT, UNROLL> &st, int win, int buf) {
-        const char *xb = x_lds + buf * x_buf_bytes + xrow * geo.x_row_bytes;
-        const uint32_t *szb = reinterpret_cast<const uint32_t *>(sz_lds + buf * sz_buf_bytes);
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int kbl = wave * UNROLL + u;             // block within the window
-            const int kb = win * WB + kbl;
-            // blocks past the end and padding quarters contribute nothing:
-            // their scale is taken as zero
-            const bool valid = kb < kblocks && !(kb == kblocks - 1 && quarter > geo.last_full_quarter);
-            f16x8 a[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                a[t] = *reinterpret_cast<const f16x8 *>(xb + (kbl * 4 + quarter) * 64 + 16 * t);
-            const int gw = ((kbl << 7) + (quarter << 5)) >> gshift;
-            if (FOLD) {
-                // X = 2^-24 * sum of this lane-row's x over the block.
-                const f16x8 tiny = bitcast<f16x8>(u32x4{0x00010001u, 0x00010001u, 0x00010001u, 0x00010001u});
-                f32x4 xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], tiny, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                for (int t = 1; t < 4; ++t) xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], tiny, xs, 0, 0, 0);
-#pragma unroll
-                for (int t = 0; t < CT; ++t) {
-                    u32x4 b0, b1, b2, b3;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t w = st.w[u][t][j];
-                        const uint32_t w8 = w >> 8;
-                        b0[j] = w & 0x000F000Fu;     // codes 0,4 as c * 2^-24
-                        b1[j] = w & 0x00F000F0u;     // codes 1,5 as c * 2^-20
-                        b2[j] = w8 & 0x000F000Fu;    // codes 2,6 as c * 2^-24
-                        b3[j] = w8 & 0x00F000F0u;    // codes 3,7 as c * 2^-20
-                    }
-                    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-                    f32x4 p24 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], bitcast<f16x8>(b0), zero4, 0, 0, 0);
-                    f32x4 p20 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], bitcast<f16x8>(b1), zero4, 0, 0, 0);
-                    p24 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], bitcast<f16x8>(b2), p24, 0, 0, 0);
-                    p20 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], bitcast<f16x8>(b3), p20, 0, 0, 0);
-                    const uint32_t sz = szb[(t * 16 + col) * geo.sz_stride + gw];
-                    const float s = valid ? half_bits_to_float((uint16_t)sz) * 16777216.0f : 0.0f;  // s * 2^24, exact
-                    const float nz = -half_bits_to_float((uint16_t)(sz >> 16));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v = __builtin_fmaf(p20[r], 0.0625f, p24[r]);
-                        acc[t][r] = __builtin_fmaf(s, __builtin_fmaf(nz, xs[r], v), acc[t][r]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < CT; ++t) {
-                    const uint32_t sz = szb[(t * 16 + col) * geo.sz_stride + gw];
-                    const _Float16 s = valid ? bitcast<_Float16>((uint16_t)sz) : (_Float16)0.0f;
-                    const _Float16 zb = bitcast<_Float16>((uint16_t)(sz >> 16)) + (_Float16)1024.0f;
-                    const f16x2 scale = {s, s}, bias = {zb, zb};
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        u32x4 b;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t h = ((st.w[u][t][j] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-                            b[j] = bitcast<uint32_t>((bitcast<f16x2>(h) - bias) * scale);
-                        }
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p], bitcast<f16x8>(b), acc[t], 0, 0, 0);
-                    }
-                }
-            }
-        }
-    };
-
-    // ---- main loop: two register stages, two LDS buffers ----
-    // The body is unrolled by two and free of data-dependent branches, so
-    // the compiler can keep the next window's loads in flight while the
-    // current one is computed (it waits only for the older stage).  The last
-    // prefetch of an even window count re-reads the final window, which is
-    // still cache-resident, instead of branching around the loads.
-    Stage<CT, UNROLL> s0, s1;
-    Coop<XC, SC> cp;
-    coop_load(cp, 0);
-    load_weights(s0, 0);
-    coop_store(cp, 0);
-    __syncthreads();
-    int win = 0;
-    for (; win + 1 < nwin; win += 2) {
-        coop_load(cp, win + 1);
-        load_weights(s1, win + 1);
-        compute(s0, win, 0);
-        coop_store(cp, 1);
-        __syncthreads();
-        const int next = min(win + 2, nwin - 1);
-        coop_load(cp, next);
-        load_weights(s0, next);
-        compute(s1, win + 1, 1);
-        coop_store(cp, 0);
-        __syncthreads();
     }
-    if (win < nwin) compute(s0, win, 0);      // odd count: the last window sits in s0 / buffer 0
-    if (SPLIT > 1) __syncthreads();           // the partial sums below reuse the x buffers
+}
 
-    // Lane l holds rows 4*(l/16) + r (r = 0..3) of column l % 16 of each tile.
+// Sum of the SPLIT waves' partial tiles (fixed order) and the fp16 store.
+// Lane l holds rows 4*(l/16) + r (r = 0..3) of column l % 16 of each tile.
+template <int SPLIT, int CT>
+__device__ __forceinline__ void finish(f32x4 acc[CT], char *lds, uint16_t *y, int m, int n_out,
+                                       int row0, int wave, int lane)
+{
+    const int col = lane & 15, quarter = lane >> 4;
     if (SPLIT > 1) {
-        f32x4 *partial = reinterpret_cast<f32x4 *>(lds);       // [SPLIT][CT][64], reuses the x buffers
+        f32x4 *partial = reinterpret_cast<f32x4 *>(lds);       // [SPLIT][CT][64]
 #pragma unroll
         for (int t = 0; t < CT; ++t) partial[(wave * CT + t) * 64 + lane] = acc[t];
         __syncthreads();
         if (wave >= CT) return;
-        // wave t finishes tile t, summing the waves in a fixed order
-        const int t = wave;
+        const int t = wave;                                     // wave t finishes tile t
         f32x4 sum = partial[t * 64 + lane];
 #pragma unroll
         for (int w = 1; w < SPLIT; ++w) sum += partial[(w * CT + t) * 64 + lane];
@@ -331,24 +195,349 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_kernel(
     }
 }
 
-template <int SPLIT, int CT, int UNROLL, bool FOLD>
-size_t lds_bytes(const Geometry &g)
+// Per-lane weight addressing shared by both kernels: a wave-uniform base
+// plus fixed 32-bit lane offsets.  Rows past n_out are clamped to a valid
+// row (their outputs are never stored).
+template <int CT>
+struct WeightAddr {
+    const char *qbase;
+    const char *xsafe;      // 16-byte-aligned, L2-hot target for loads past the end
+    uint32_t woff[CT];
+    int quarter, kblocks, last_full_quarter;
+
+    __device__ __forceinline__ void init(const uint32_t *qweight, const uint16_t *x,
+                                         const Geometry &geo, int row0, int col, int q)
+    {
+        qbase = reinterpret_cast<const char *>(qweight + (int64_t)row0 * geo.words_per_row);
+        xsafe = reinterpret_cast<const char *>(x);
+        quarter = q;
+        kblocks = geo.kblocks;
+        last_full_quarter = geo.last_full_quarter;
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            const int r = min(t * 16 + col, geo.n_out - 1 - row0);
+            woff[t] = (uint32_t)(r * geo.words_per_row + q * 4) * 4u;
+        }
+    }
+    // A block past the end, or a padding quarter of a partial last block.
+    __device__ __forceinline__ bool valid(int kb) const
+    {
+        return kb < kblocks && !(kb == kblocks - 1 && quarter > last_full_quarter);
+    }
+    __device__ __forceinline__ u32x4 load(int kb, int t) const
+    {
+        // a padding quarter is moved back onto the last whole slice; the
+        // offsets are summed as 32-bit values before meeting the base, so the
+        // wrapped negative part cancels
+        const int qs = (kb == kblocks - 1 && quarter > last_full_quarter) ? last_full_quarter - quarter : 0;
+        const bool inside = kb < kblocks;
+        const uint32_t off = inside ? woff[t] + (uint32_t)(kb * 16 + qs * 4) * 4u : 0u;
+        const char *base = inside ? qbase : xsafe;
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + off));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Resident kernel: x and all scale|zero pairs staged once in LDS.
+// ---------------------------------------------------------------------------
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD>
+__global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    uint16_t *__restrict__ y, Geometry geo)
 {
-    const size_t x_region = 2 * (size_t)g.m * g.x_row_bytes;
-    const size_t partial = SPLIT > 1 ? (size_t)SPLIT * CT * 64 * 16 : 0;
-    return (x_region > partial ? x_region : partial) + 2 * (size_t)16 * CT * g.sz_stride * 4;
+    constexpr int THREADS = 64 * SPLIT;
+    constexpr int ROWS = 16 * CT;
+    constexpr int SB = SPLIT * UNROLL;             // blocks per stage
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+
+    const int m = geo.m, n_out = geo.n_out, n_in = geo.n_in, gshift = geo.group_shift;
+    const int kblocks = geo.kblocks, G = geo.groups_per_row;
+    const int x_bytes = m * geo.x_row_bytes;
+    const int part_bytes = SPLIT > 1 ? SPLIT * CT * 1024 : 0;
+    char *x_lds = lds;
+    uint32_t *sz_lds = reinterpret_cast<uint32_t *>(lds + max(x_bytes, part_bytes));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int quarter = lane >> 4;
+    const int row0 = blockIdx.x * ROWS;
+
+    WeightAddr<CT> wa;
+    wa.init(qweight, x, geo, row0, col, quarter);
+    auto load_stage = [&](Stage<CT, UNROLL> &st, int i) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int t = 0; t < CT; ++t) st.w[u][t] = wa.load((i * SPLIT + wave) * UNROLL + u, t);
+    };
+
+    // ---- staging of x (chunk c = (row, block, quarter) holds 32 values) and
+    // of the scale|zero pairs of rows row0 .. row0 + ROWS.  The first batch
+    // of staging loads is issued before the first DEPTH-1 weight stages, so
+    // the LDS stores below wait only for the (cache-hot) staging data while
+    // the weights stay in flight across the barrier.
+    const int nstages = (kblocks + SB - 1) / SB;
+    const int n_chunks = m * kblocks * 4;
+    const int n_items = ROWS * G;
+    const bool sz_vec = geo.sz_vector && row0 + ROWS <= n_out;
+    const u32x4 *sv = reinterpret_cast<const u32x4 *>(scales + (int64_t)row0 * G);
+    const u32x4 *zv = reinterpret_cast<const u32x4 *>(zeros + (int64_t)row0 * G);
+
+    auto x_load = [&](int c, u32x4 v[4]) {
+        c = min(c, n_chunks - 1);
+        const int r = c / (kblocks * 4), rem = c % (kblocks * 4);
+        const int k = min(rem * 32, n_in - 32);          // padding quarters repeat a valid slice
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (int64_t)r * n_in + k);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = src[j];
+    };
+    auto x_store = [&](int c, const u32x4 v[4]) {
+        if (c < n_chunks) {
+            const int r = c / (kblocks * 4), rem = c % (kblocks * 4);
+            store_x_chunk(x_lds + r * geo.x_row_bytes + (rem >> 2) * 256, rem & 3, v);
+        }
+    };
+    // vector path: the rows are one contiguous, 16-byte-aligned run of both
+    // arrays, 8 pairs per chunk; otherwise one pair per item
+    auto sz_load = [&](int c, u32x4 &s8, u32x4 &z8) {
+        if (sz_vec) {
+            c = min(c, n_items / 8 - 1);
+            s8 = sv[c];
+            z8 = zv[c];
+        } else {
+            c = min(c, n_items - 1);
+            const int r = c / G, g = c - r * G;
+            const int64_t off = (int64_t)min(row0 + r, n_out - 1) * G + g;
+            s8 = u32x4{(uint32_t)scales[off], 0u, 0u, 0u};
+            z8 = u32x4{(uint32_t)zeros[off], 0u, 0u, 0u};
+        }
+    };
+    auto sz_store = [&](int c, const u32x4 &s8, const u32x4 &z8) {
+        if (sz_vec) {
+            if (c < n_items / 8) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = c * 8 + i, r = e / G, g = e - r * G;
+                    const uint32_t sh = (s8[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    const uint32_t zh = (z8[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    sz_lds[r * geo.sz_stride + g] = sh | (zh << 16);
+                }
+            }
+        } else if (c < n_items) {
+            const int r = c / G, g = c - r * G;
+            sz_lds[r * geo.sz_stride + g] = s8[0] | (z8[0] << 16);
+        }
+    };
+    const int sz_units = sz_vec ? n_items / 8 : n_items;
+
+    u32x4 xv[4], s8, z8;
+    x_load(tid, xv);
+    sz_load(tid, s8, z8);
+    Stage<CT, UNROLL> ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) load_stage(ring[d], d);
+    x_store(tid, xv);
+    sz_store(tid, s8, z8);
+    for (int c = tid + THREADS; c < n_chunks; c += THREADS) {
+        x_load(c, xv);
+        x_store(c, xv);
+    }
+    for (int c = tid + THREADS; c < sz_units; c += THREADS) {
+        sz_load(c, s8, z8);
+        sz_store(c, s8, z8);
+    }
+    __syncthreads();
+
+    f32x4 acc[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char *xrow = x_lds + min(col, m - 1) * geo.x_row_bytes;
+    const uint32_t *szrow = sz_lds + col * geo.sz_stride;
+    auto compute = [&](const Stage<CT, UNROLL> &st, int i) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int kb = (i * SPLIT + wave) * UNROLL + u;
+            const int kbc = min(kb, kblocks - 1);
+            f16x8 a[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                a[t] = *reinterpret_cast<const f16x8 *>(xrow + kbc * 256 + t * 64 + quarter * 16);
+            // a padding quarter of a partial last block reads the last real
+            // group (its contribution is masked), never past the row
+            const int qe = (kbc == kblocks - 1) ? min(quarter, geo.last_full_quarter) : quarter;
+            const int g = ((kbc << 7) + (qe << 5)) >> gshift;
+            uint32_t sz[CT];
+#pragma unroll
+            for (int t = 0; t < CT; ++t) sz[t] = szrow[t * 16 * geo.sz_stride + g];
+            process_block<CT, FOLD>(acc, a, st.w[u], sz, wa.valid(kb));
+        }
+    };
+
+    // ---- stream the weights through the register ring ----
+    for (int i0 = 0; i0 < nstages; i0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int i = i0 + d;
+            load_stage(ring[(d + DEPTH - 1) % DEPTH], i + DEPTH - 1);
+            if (i < nstages) compute(ring[d], i);
+        }
+    }
+    if (SPLIT > 1) __syncthreads();           // the partial sums reuse the x buffer
+    finish<SPLIT, CT>(acc, lds, y, m, n_out, row0, wave, lane);
 }
 
-constexpr size_t kMaxLds = 64 * 1024;
+// ---------------------------------------------------------------------------
+// Windowed kernel: x and scale|zero pairs staged one window ahead.
+// ---------------------------------------------------------------------------
+template <int XC, int SC>
+struct Coop {
+    u32x4 x[XC][4];
+    uint16_t s[SC], z[SC];
+};
 
-template <int SPLIT, int CT, int UNROLL, bool FOLD>
-bool plan(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
-          const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
-          uint16_t *y, hipStream_t stream, hipError_t *err)
+template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX>
+__global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    uint16_t *__restrict__ y, Geometry geo)
 {
-    static_assert(SPLIT >= CT || SPLIT == 1, "the LDS reduction assigns one wave per tile");
-    static_assert(SPLIT * UNROLL % 2 == 0, "a window must hold whole groups of 256");
-    constexpr int WB = SPLIT * UNROLL;
+    constexpr int THREADS = 64 * SPLIT;
+    constexpr int WB = SPLIT * UNROLL;          // k blocks per window
+    constexpr int ROWS = 16 * CT;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+
+    const int m = geo.m, n_out = geo.n_out, n_in = geo.n_in, gshift = geo.group_shift;
+    const int kblocks = geo.kblocks;
+    const int groups_win = (WB * 128) >> gshift;
+    const int x_buf_bytes = m * geo.x_row_bytes;
+    const int sz_buf_bytes = ROWS * geo.sz_stride * 4;
+    char *x_lds = lds;                                   // [2][m][x_row_bytes]
+    char *sz_lds = lds + 2 * x_buf_bytes;                // [2][ROWS][sz_stride] u32
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int quarter = lane >> 4;
+    const int row0 = blockIdx.x * ROWS;
+    const int nwin = (kblocks + WB - 1) / WB;
+
+    WeightAddr<CT> wa;
+    wa.init(qweight, x, geo, row0, col, quarter);
+    auto load_weights = [&](Stage<CT, UNROLL> &st, int win) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int t = 0; t < CT; ++t) st.w[u][t] = wa.load(win * WB + wave * UNROLL + u, t);
+    };
+
+    constexpr int MAX_XCHUNKS = MMAX * WB * 4;             // m <= MMAX rows
+    constexpr int XC = (MAX_XCHUNKS + THREADS - 1) / THREADS;
+    constexpr int MAX_SITEMS = ROWS * WB * 4;              // group_size >= 32
+    constexpr int SC = (MAX_SITEMS + THREADS - 1) / THREADS;
+    const int n_xchunks = m * WB * 4;
+    const int n_sitems = ROWS * groups_win;
+    auto coop_load = [&](Coop<XC, SC> &c, int win) {
+        // windows past the end re-read the last one (small, cache-resident)
+        const int wv = min(win, nwin - 1);
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int cc = min(tid + i * THREADS, n_xchunks - 1);
+            const int r = cc / (WB * 4), rem = cc % (WB * 4);
+            const int kb = min(wv * WB + rem / 4, kblocks - 1);
+            const int k = min((kb << 7) + ((rem & 3) << 5), n_in - 32);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (int64_t)r * n_in + k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c.x[i][j] = src[j];
+        }
+#pragma unroll
+        for (int i = 0; i < SC; ++i) {
+            const int it = min(tid + i * THREADS, n_sitems - 1);
+            const int r = min(row0 + it / groups_win, n_out - 1);
+            const int gidx = min(wv * groups_win + it % groups_win, geo.groups_per_row - 1);
+            const int64_t off = (int64_t)r * geo.groups_per_row + gidx;
+            c.s[i] = scales[off];
+            c.z[i] = zeros[off];
+        }
+    };
+    auto coop_store = [&](const Coop<XC, SC> &c, int buf) {
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int ch = tid + i * THREADS;
+            if (ch < n_xchunks) {
+                const int r = ch / (WB * 4), rem = ch % (WB * 4);     // rem = block * 4 + quarter
+                store_x_chunk(x_lds + buf * x_buf_bytes + r * geo.x_row_bytes + (rem >> 2) * 256, rem & 3,
+                              c.x[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SC; ++i) {
+            const int it = tid + i * THREADS;
+            if (it < n_sitems) {
+                const int r = it / groups_win, gw = it % groups_win;
+                reinterpret_cast<uint32_t *>(sz_lds + buf * sz_buf_bytes)[r * geo.sz_stride + gw] =
+                    (uint32_t)c.s[i] | ((uint32_t)c.z[i] << 16);
+            }
+        }
+    };
+
+    f32x4 acc[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int xr = min(col, m - 1);
+    auto compute = [&](const Stage<CT, UNROLL> &st, int win, int buf) {
+        const char *xb = x_lds + buf * x_buf_bytes + xr * geo.x_row_bytes;
+        const uint32_t *szb = reinterpret_cast<const uint32_t *>(sz_lds + buf * sz_buf_bytes) + col * geo.sz_stride;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int kbl = wave * UNROLL + u;             // block within the window
+            f16x8 a[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                a[t] = *reinterpret_cast<const f16x8 *>(xb + kbl * 256 + t * 64 + quarter * 16);
+            const int gw = ((kbl << 7) + (quarter << 5)) >> gshift;
+            uint32_t sz[CT];
+#pragma unroll
+            for (int t = 0; t < CT; ++t) sz[t] = szb[t * 16 * geo.sz_stride + gw];
+            process_block<CT, FOLD>(acc, a, st.w[u], sz, wa.valid(win * WB + kbl));
+        }
+    };
+
+    // Two register stages, two LDS buffers; the body is unrolled by two and
+    // its loads are unconditional (past the end they are redirected), so the
+    // compiler waits only for the older stage.
+    Stage<CT, UNROLL> s0, s1;
+    Coop<XC, SC> cp;
+    coop_load(cp, 0);
+    load_weights(s0, 0);
+    coop_store(cp, 0);
+    __syncthreads();
+    for (int win = 0; win < nwin; win += 2) {
+        coop_load(cp, win + 1);
+        load_weights(s1, win + 1);
+        compute(s0, win, 0);
+        coop_store(cp, 1);
+        __syncthreads();
+        if (win + 1 >= nwin) break;
+        coop_load(cp, win + 2);
+        load_weights(s0, win + 2);
+        compute(s1, win + 1, 1);
+        coop_store(cp, 0);
+        __syncthreads();
+    }
+    finish<SPLIT, CT>(acc, lds, y, m, n_out, row0, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Launch planning.
+// ---------------------------------------------------------------------------
+constexpr size_t kMaxLds = 160 * 1024;     // per workgroup on gfx950
+
+Geometry make_geometry(int m, int n_out, int n_in, int group_shift)
+{
     Geometry g;
     g.m = m;
     g.n_out = n_out;
@@ -358,19 +547,86 @@ bool plan(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
     g.groups_per_row = n_in >> group_shift;
     g.kblocks = (n_in + 127) >> 7;
     g.last_full_quarter = ((n_in - ((g.kblocks - 1) << 7)) >> 5) - 1;
-    g.sz_stride = ((WB * 128) >> group_shift) | 1;
-    g.x_row_bytes = WB * 256 + 16;
-    const size_t lds = lds_bytes<SPLIT, CT, UNROLL, FOLD>(g);
-    if (lds > kMaxLds) return false;           // x window too large for this m
+    g.sz_stride = 0;
+    g.x_row_bytes = 0;
+    g.sz_vector = 0;
+    return g;
+}
+
+template <typename K>
+hipError_t allow_full_lds(K kernel)
+{
+    // once per kernel instantiation (thread-safe static initialization)
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    (int)kMaxLds);
+    return e;
+}
+
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD>
+bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                   const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
+                   uint16_t *y, hipStream_t stream, hipError_t *err)
+{
+    static_assert(SPLIT >= CT || SPLIT == 1, "the LDS reduction assigns one wave per tile");
+    Geometry g = make_geometry(m, n_out, n_in, group_shift);
+    g.sz_stride = g.groups_per_row | 1;
+    g.x_row_bytes = g.kblocks * 256 + 16;
+    g.sz_vector = ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 15) == 0 &&
+                  (16 * CT * g.groups_per_row) % 8 == 0;
+    const size_t x_bytes = (size_t)m * g.x_row_bytes;
+    const size_t part = SPLIT > 1 ? (size_t)SPLIT * CT * 1024 : 0;
+    const size_t lds = (x_bytes > part ? x_bytes : part) + (size_t)16 * CT * g.sz_stride * 4;
+    if (lds > kMaxLds) return false;
+    auto kernel = gemv_resident_kernel<SPLIT, CT, UNROLL, DEPTH, FOLD>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = allow_full_lds(kernel);
+        if (e != hipSuccess) {
+            *err = e;
+            return true;
+        }
+    }
     const int tiles = (n_out + 15) / 16;
     const dim3 grid((unsigned)((tiles + CT - 1) / CT)), block(64 * SPLIT);
-    gemv_kernel<SPLIT, CT, UNROLL, FOLD><<<grid, block, lds, stream>>>(x, qweight, scales, zeros, y, g);
+    kernel<<<grid, block, lds, stream>>>(x, qweight, scales, zeros, y, g);
     *err = hipGetLastError();
     return true;
 }
 
-// Deep windows for long rows, shallower ones when m makes the x window
-// large or the rows are short.
+template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX>
+bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                 const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
+                 uint16_t *y, hipStream_t stream, hipError_t *err)
+{
+    static_assert(SPLIT >= CT || SPLIT == 1, "the LDS reduction assigns one wave per tile");
+    static_assert(SPLIT * UNROLL % 2 == 0, "a window must hold whole groups of 256");
+    constexpr int WB = SPLIT * UNROLL;
+    if (m > MMAX) return false;
+    Geometry g = make_geometry(m, n_out, n_in, group_shift);
+    g.sz_stride = ((WB * 128) >> group_shift) | 1;
+    g.x_row_bytes = WB * 256 + 16;
+    const size_t x_region = 2 * (size_t)m * g.x_row_bytes;
+    const size_t part = SPLIT > 1 ? (size_t)SPLIT * CT * 1024 : 0;
+    const size_t lds = (x_region > part ? x_region : part) + 2 * (size_t)16 * CT * g.sz_stride * 4;
+    if (lds > kMaxLds) return false;
+    auto kernel = gemv_window_kernel<SPLIT, CT, UNROLL, FOLD, MMAX>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = allow_full_lds(kernel);
+        if (e != hipSuccess) {
+            *err = e;
+            return true;
+        }
+    }
+    const int tiles = (n_out + 15) / 16;
+    const dim3 grid((unsigned)((tiles + CT - 1) / CT)), block(64 * SPLIT);
+    kernel<<<grid, block, lds, stream>>>(x, qweight, scales, zeros, y, g);
+    *err = hipGetLastError();
+    return true;
+}
+
+// Configurations chosen from measured sweeps on MI355X over the decode
+// shapes (7B and 70B projections, m = 1 and 8); other shapes fall through to
+// the nearest rule.  Every rule ends in a configuration that always fits.
 template <bool FOLD>
 hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
@@ -378,20 +634,32 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
 {
     hipError_t e = hipSuccess;
     const int kblocks = (n_in + 127) >> 7;
-#define Q4_TRY(S, C, U) \
-    if (plan<S, C, U, FOLD>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
-    if (kblocks >= 32) {
-        Q4_TRY(8, 2, 2);
-        Q4_TRY(8, 2, 1);
-        Q4_TRY(4, 2, 1);
+    const int tiles = (n_out + 15) / 16;
+#define Q4_RES(S, C, U, D) \
+    if (plan_resident<S, C, U, D, FOLD>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+#define Q4_WIN(S, C, U, MM) \
+    if (plan_window<S, C, U, FOLD, MM>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+    if (kblocks >= 16) {
+        if (!FOLD) {
+            Q4_RES(16, 1, 1, 4);
+        } else if (m == 1) {
+            if (tiles <= 256) Q4_RES(16, 1, 1, 2);
+            if (kblocks >= 128 && tiles >= 512) Q4_RES(8, 2, 1, 2);
+            if (tiles <= 768) Q4_RES(8, 1, 1, 2);
+            Q4_RES(4, 2, 1, 4);
+        } else {
+            if (tiles >= 640) Q4_RES(16, 4, 1, 2);
+            if (tiles >= 256) Q4_RES(8, 2, 1, 2);
+            Q4_RES(8, 1, 1, 2);
+        }
+        if (m <= 8) Q4_WIN(16, 2, 1, 8);
+        Q4_WIN(8, 2, 1, 16);
     }
-    if (kblocks >= 8) {
-        Q4_TRY(4, 2, 2);
-        Q4_TRY(4, 2, 1);
-    }
-    Q4_TRY(1, 1, 2);
-#undef Q4_TRY
-    return hipErrorInvalidValue;                // unreachable for m <= 16
+    Q4_RES(4, 1, 1, 2);
+    Q4_WIN(2, 1, 1, 16);
+#undef Q4_RES
+#undef Q4_WIN
+    return hipErrorInvalidValue;                // unreachable: the last window always fits
 }
 
 }  // namespace
