@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("m", [1, 17, 64, 127, 128, 129, 300])
 @pytest.mark.parametrize("n_out,n_in,g", [(1, 32, 32), (100, 96, 32), (128, 256, 128),
-                                          (300, 4096, 128), (129, 1088, 64), (64, 512, 256)])
+                                          (300, 4096, 128), (129, 1088, 64), (64, 512, 256),
+                                          (200, 1120, 32), (64, 160, 32), (48, 192, 64)])
 def test_gemm_shapes(orc, m, n_out, n_in, g):
     w = synthetic.normal_weight(n_out, n_in, seed=n_out + 3 * n_in, std=0.02,
                                 n_outlier_cols=synthetic.n_outliers(n_in))

@@ -2,134 +2,261 @@
 //
 // [Guide] §2.3: W4A16 turns the INT4 weights back into FP16 before the
 // matrix product, so at prefill sizes the layer is bound by the fp16 matrix
-// cores, not by memory.  The kernel therefore dequantizes each packed weight
-// tile once into LDS as fp16 and lets every wave of the workgroup reuse it
-// from there with v_mfma_f32_32x32x16_f16 (fp32 accumulation).
+// cores, not by memory.  The kernel dequantizes each packed weight tile once
+// into LDS as fp16 and lets every wave of the workgroup reuse it from there
+// with v_mfma_f32_32x32x16_f16 (fp32 accumulation).
 //
-// Tiling.  A workgroup computes a BM x BN tile of y with WAVES_M x WAVES_N
-// waves; each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32x32
-// MFMA tiles.  Per BK-wide k step the workgroup
-//   * loads the x tile (BM x BK fp16, 16-byte chunks, 8 lanes per 128-byte
-//     row run) and the packed weight tile (BN x BK codes, 16 bytes = 32 codes
-//     per lane, all in one group) into registers,
-//   * stores x into LDS and the dequantized weights s (c - z) as fp16 into
-//     LDS, both in the pair order produced by the code unpacking,
-//   * runs the MFMAs out of LDS while the next tile's global loads are in
-//     flight.
-// LDS rows are padded by 8 halves (16 bytes) so the 32 rows read by one
-// 16-byte-per-lane fragment load fall on distinct bank groups.
+// Tiling.  A workgroup computes a BM x BN tile of y (BM rows of x, BN output
+// channels) with WM x WN waves, one wave per SIMD; each wave owns a
+// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  k advances in steps
+// of 64 = four MFMA substeps of 16.
+//
+// Software pipeline (one wave per SIMD, so every latency has to be covered
+// by the wave's own instruction stream):
+//   * three LDS stages: step k computes from stage k%3 while its stores fill
+//     stage (k+2)%3 and stage (k+1)%3, published by the previous barrier,
+//     already serves the first fragments of step k+1; one barrier per step;
+//   * two fragment register sets: substep s+1's A/B fragments are read from
+//     LDS while substep s runs its MFMAs;
+//   * three global register sets: the x chunks and packed words of step
+//     k+2 are loaded during step k-3 and written to LDS during step k (x
+//     unchanged, weights dequantized to fp16 s * (c - z)), a quarter per
+//     substep, each quarter's registers reloaded right after with step
+//     k+5's data, so every load has about three steps to arrive;
+//   * scheduling group barriers interleave each substep's LDS reads, LDS
+//     writes, dequantization arithmetic and global loads between its MFMAs.
+// The stage and register-set rotations both have period three, so the loop
+// is unrolled three times and every LDS address is a lane constant plus an
+// immediate.  Global loads are buffer loads: a per-tile resource, a
+// lane-constant 32-bit offset and a uniform per-step offset.  The pipelined
+// loop covers the full 64-wide steps; n_in % 64 == 32 leaves one 32-wide
+// step, done afterwards without pipelining.
+//
+// LDS rows are 128 bytes (64 halves); the eight 16-byte chunks of row r are
+// stored at chunk ^ swz(r) (see below) so that fragment reads (16 rows, one
+// chunk each), x stores (whole rows) and weight stores (8 rows, two half-rows
+// of 4 chunks each) all hit distinct 16-byte bank groups, whether the lanes
+// are served 8 at a time over 32 banks or 16 at a time over 64 banks.
 //
 // The grid is linear; workgroup ids are dealt round-robin to the eight XCDs,
-// so ids are remapped to give each XCD a contiguous band of tiles, and tiles
-// are walked column-band by column-band so consecutive workgroups on an XCD
-// share weight tiles in its L2.
+// so ids are remapped to give each XCD a contiguous range of tiles.  Tiles
+// are numbered in bands of kGroupM row tiles, walked output-column by
+// output-column inside a band, so an XCD's range covers few row tiles of x
+// (BM rows x n_in fp16 each, the larger operand) and many column tiles of
+// the packed weights (BN rows x n_in/2 bytes each), which its L2 shares.
+#include <type_traits>
+
 #include "q4_device.h"
 #include "q4_launch.h"
 
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kStages = 3;
+constexpr int kGroupM = 2;
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
+constexpr int kBufferFlags = 0x00020000;
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100,
+              kSgDsWrite = 0x200;
+
+// Eight codes of one packed word -> eight fp16 weights s * (c - z) in
+// natural order (c0, c1), (c2, c3), ...: the codes are split into even and
+// odd nibbles, byte-permuted next to a zero byte and OR-ed into the half
+// 1024 (0x6400); (1024 + c) - (1024 + z) is exact and the product with s is
+// the only rounding.
+__device__ __forceinline__ u32x4 dequant_word_natural(uint32_t w, f16x2 bias, f16x2 scale)
+{
+    const uint32_t lo = w & 0x0F0F0F0Fu;           // c0 c2 c4 c6
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;    // c1 c3 c5 c7
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x64006400u;
+    r[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x64006400u;
+    r[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x64006400u;
+    r[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x64006400u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = bitcast<uint32_t>((bitcast<f16x2>(r[j]) - bias) * scale);
+    return r;
+}
+
+// Chunk permutation of LDS row r, a function of r & 15.  Its low two bits
+// differ across any 4 consecutive rows and across the 4 even (or 4 odd) rows
+// of an aligned group of 8; the whole value differs across any aligned group
+// of 8 rows and across the 8 even (or 8 odd) rows of an aligned group of 16.
+__device__ __forceinline__ int swz(int r)
+{
+    return ((r ^ (r >> 2)) & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+}
+
+// Scheduling pattern of one substep: each of its N MFMAs is followed by one
+// LDS read (the first NDSR slots), NVALU vector ALU instructions, one LDS
+// write (the last NDSW slots) and one global load (the first NVMEM slots).
+template <int I, int N, int NDSR, int NDSW, int NVMEM, int NVALU>
+__device__ __forceinline__ void interleave()
+{
+    if constexpr (I < N) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if constexpr (I < NDSR) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        if constexpr (NVALU > 0) __builtin_amdgcn_sched_group_barrier(kSgValu, NVALU, 0);
+        if constexpr (I >= N - NDSW) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
+        if constexpr (I < NVMEM) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+        interleave<I + 1, N, NDSR, NDSW, NVMEM, NVALU>();
+    }
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     uint16_t *__restrict__ y, int m, int n_out, int n_in, int group_shift,
     int tiles_m, int tiles_n)
 {
-    constexpr int THREADS = 64 * WAVES_M * WAVES_N;
-    constexpr int WT_M = BM / WAVES_M, WT_N = BN / WAVES_N;
+    constexpr int BK = 64, KSUB = BK / 16;
+    constexpr int NW = WM * WN, THREADS = 64 * NW;
+    constexpr int WT_M = BM / WM, WT_N = BN / WN;
     constexpr int TM = WT_M / 32, TN = WT_N / 32;
-    constexpr int LDK = BK + 8;
-    constexpr int A_CHUNKS = BM * BK / 8 / THREADS;     // 16-byte x chunks per lane
-    constexpr int B_SLICES = BN * BK / 32 / THREADS;    // 16-byte code slices per lane
-    static_assert(A_CHUNKS * THREADS * 8 == BM * BK, "x tile does not split evenly");
-    static_assert(B_SLICES * THREADS * 32 == BN * BK, "weight tile does not split evenly");
+    constexpr int A_CHUNKS = BM * 8 / THREADS;         // 16-byte x chunks per lane per step
+    constexpr int B_SLICES = BN * 2 / THREADS;         // 16-byte code slices per lane per step
+    constexpr int A_PART = A_CHUNKS / KSUB;            // x chunks stored per substep
+    constexpr int B_PART = B_SLICES;                   // packed words dequantized per substep
+    static_assert(A_CHUNKS * THREADS == BM * 8 && A_PART * KSUB == A_CHUNKS,
+                  "x tile does not split evenly");
+    static_assert(B_SLICES * THREADS == BN * 2, "weight tile does not split evenly");
     static_assert(TM * 32 == WT_M && TN * 32 == WT_N, "wave tile not a multiple of 32");
-
-    __shared__ __attribute__((aligned(16))) _Float16 As[BM * LDK];
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[BN * LDK];
+    static_assert(THREADS % 128 == 0, "row swizzles assume 16-row lane strides");
+    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
+    static_assert(kStages * STAGE <= 160 * 1024, "stages exceed LDS");
+    extern __shared__ __attribute__((aligned(16))) char smem[];   // [kStages][A | B]
 
     // --- tile selection (XCD-aware) ---
     const int tiles = tiles_m * tiles_n;
     const int bid = blockIdx.x;
-    const int per_xcd = (tiles + kXcds - 1) / kXcds;
-    const int xcd = bid % kXcds;
-    int t = xcd * per_xcd + bid / kXcds;
-    // The last band may be short; ids past the end fold back onto the tiles
-    // no band covered (bands are contiguous, so this is a bijection).
-    if (tiles % kXcds != 0) {
-        const int full = tiles % kXcds;       // bands with per_xcd tiles
-        t = (xcd < full) ? xcd * per_xcd + bid / kXcds
-                         : full * per_xcd + (xcd - full) * (per_xcd - 1) + bid / kXcds;
-    }
-    const int tile_n = t / tiles_m;
-    const int tile_m = t % tiles_m;
+    const int xcd = bid % kXcds, local = bid / kXcds;
+    const int per_xcd = tiles / kXcds, extra = tiles % kXcds;
+    // XCDs 0..extra-1 own per_xcd + 1 consecutive tiles, the rest per_xcd
+    const int t = xcd < extra ? xcd * (per_xcd + 1) + local
+                              : extra * (per_xcd + 1) + (xcd - extra) * per_xcd + local;
+    const int band = t / (kGroupM * tiles_n);
+    const int band_m = min(kGroupM, tiles_m - band * kGroupM);
+    const int in_band = t - band * kGroupM * tiles_n;
+    const int tile_n = in_band / band_m;
+    const int tile_m = band * kGroupM + in_band % band_m;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wave_m = wave / WAVES_N, wave_n = wave % WAVES_N;
-
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave / WN, wave_n = wave % WN;
     const int words_per_row = n_in >> 3;
     const int groups_per_row = n_in >> group_shift;
+    const int ksteps = n_in / BK;                       // full 64-wide steps
 
-    // --- per-lane global load coordinates ---
-    int a_row[A_CHUNKS], a_col[A_CHUNKS];
+    // Per-tile buffer resources covering the tile's rows; lanes add constant
+    // 32-bit byte offsets (a tile spans at most 256 rows of at most 2^20
+    // halves, so every offset stays below 2^30).  Rows past m or n_out read
+    // the last row: they are never stored.
+    const int rows_m = min(BM, m - m0), rows_n = min(BN, n_out - n0);
+    const char *xg = reinterpret_cast<const char *>(x + (int64_t)m0 * n_in);
+    const char *wg = reinterpret_cast<const char *>(qweight + (int64_t)n0 * words_per_row);
+    const char *sg = reinterpret_cast<const char *>(scales + (int64_t)n0 * groups_per_row);
+    const char *zg = reinterpret_cast<const char *>(zeros + (int64_t)n0 * groups_per_row);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(xg), (short)0, rows_m * n_in * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t wr_ = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(wg), (short)0, rows_n * words_per_row * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(sg), (short)0, rows_n * groups_per_row * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(zg), (short)0, rows_n * groups_per_row * 2, kBufferFlags);
+    uint32_t xoff[A_CHUNKS], woff[B_SLICES], soff[B_SLICES];
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-        const int c = tid + i * THREADS;
-        a_row[i] = c / (BK / 8);
-        a_col[i] = (c % (BK / 8)) * 8;
+        const int c = tid + i * THREADS;                   // row c/8, chunk c%8
+        const int r = min(c >> 3, m - 1 - m0);
+        xoff[i] = (uint32_t)r * (uint32_t)n_in * 2u + (uint32_t)(c & 7) * 16u;
     }
-    int b_row[B_SLICES], b_col[B_SLICES];
 #pragma unroll
     for (int i = 0; i < B_SLICES; ++i) {
-        const int c = tid + i * THREADS;
-        b_row[i] = c / (BK / 32);
-        b_col[i] = (c % (BK / 32)) * 32;
+        const int c = tid + i * THREADS;                   // row c/2, half c%2
+        const int r = min(c >> 1, n_out - 1 - n0);
+        woff[i] = (uint32_t)r * (uint32_t)words_per_row * 4u + (uint32_t)(c & 1) * 16u;
+        soff[i] = ((uint32_t)r * (uint32_t)groups_per_row + (uint32_t)(((c & 1) * 32) >> group_shift)) * 2u;
     }
-
-    u32x4 a_reg[A_CHUNKS];
-    u32x4 b_reg[B_SLICES];
-    uint16_t s_reg[B_SLICES], z_reg[B_SLICES];
-
-    auto load_tile = [&](int k0) {
+    // LDS byte offsets within a stage: x chunk i of this lane, weight chunk
+    // j of slice i, fragment rows.  Rows of chunk i differ by multiples of 16
+    // from those of chunk 0, so they share its swizzle.
+    const int a_row = tid >> 3, b_row = tid >> 1, b_half = tid & 1;
+    const uint32_t a_st = a_row * 128 + (((tid & 7) ^ swz(a_row)) * 16);
+    uint32_t b_st[4];
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int r = m0 + a_row[i], k = k0 + a_col[i];
-            a_reg[i] = u32x4{0u, 0u, 0u, 0u};
-            if (r < m && k < n_in)
-                a_reg[i] = *reinterpret_cast<const u32x4 *>(x + (int64_t)r * n_in + k);
-        }
-#pragma unroll
-        for (int i = 0; i < B_SLICES; ++i) {
-            const int r = n0 + b_row[i], k = k0 + b_col[i];
-            b_reg[i] = u32x4{0u, 0u, 0u, 0u};
-            s_reg[i] = 0;
-            z_reg[i] = 0;
-            if (r < n_out && k < n_in) {
-                b_reg[i] = *reinterpret_cast<const u32x4 *>(qweight + (int64_t)r * words_per_row + (k >> 3));
-                s_reg[i] = scales[(int64_t)r * groups_per_row + (k >> group_shift)];
-                z_reg[i] = zeros[(int64_t)r * groups_per_row + (k >> group_shift)];
-            }
-        }
+    for (int j = 0; j < 4; ++j) b_st[j] = A_BYTES + b_row * 128 + (((b_half * 4 + j) ^ swz(b_row)) * 16);
+    const int frow = lane & 31, fkg = lane >> 5, fswz = swz(frow);
+    const uint32_t fa = (wave_m * WT_M + frow) * 128, fb = A_BYTES + (wave_n * WT_N + frow) * 128;
+
+    struct Regs {
+        u32x4 a[A_CHUNKS];
+        u32x4 w[B_SLICES];
+        uint32_t s[B_SLICES], z[B_SLICES];
+    };
+    struct Frag {
+        f16x8 a[TM], b[TN];
     };
 
-    auto store_tile = [&]() {
+    // Global loads of step kt (kt < ksteps): x chunks of substep part p, or
+    // the packed words with their scales and zero-points.
+    auto load_a = [&](Regs &g, int kt, int p) {
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i)
-            *reinterpret_cast<f16x8 *>(&As[a_row[i] * LDK + a_col[i]]) = pair_order(a_reg[i]);
+        for (int q = 0; q < A_PART; ++q) {
+            const int i = p * A_PART + q;
+            g.a[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * (BK * 2), 0);
+        }
+    };
+    auto load_b = [&](Regs &g, int kt) {
+        const int gk = ((kt * BK) >> group_shift) * 2;
 #pragma unroll
         for (int i = 0; i < B_SLICES; ++i) {
-            const _Float16 s = bitcast<_Float16>(s_reg[i]);
-            const _Float16 zb = bitcast<_Float16>(z_reg[i]) + (_Float16)1024.0f;
-            const f16x2 scale = {s, s}, bias = {zb, zb};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<f16x8 *>(&Bs[b_row[i] * LDK + b_col[i] + 8 * j]) =
-                    dequant8_f16(b_reg[i][j], bias, scale);
+            g.w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK / 2), 0);
+            g.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff[i], gk, 0);
+            g.z[i] = __builtin_amdgcn_raw_buffer_load_b16(zr, soff[i], gk, 0);
         }
+    };
+    auto load_all = [&](Regs &g, int kt) {
+#pragma unroll
+        for (int p = 0; p < KSUB; ++p) load_a(g, kt, p);
+        load_b(g, kt);
+    };
+    // Part p of writing a step's registers into the stage at byte offset buf.
+    auto store_part = [&](const Regs &g, uint32_t buf, int p) {
+#pragma unroll
+        for (int q = 0; q < A_PART; ++q) {
+            const int i = p * A_PART + q;
+            *reinterpret_cast<u32x4 *>(smem + buf + a_st + i * THREADS * 16) = g.a[i];
+        }
+#pragma unroll
+        for (int q = 0; q < B_PART; ++q) {
+            const int wd = p * B_PART + q, i = wd >> 2, j = wd & 3;
+            const _Float16 sv = bitcast<_Float16>((uint16_t)g.s[i]);
+            const _Float16 zb = bitcast<_Float16>((uint16_t)g.z[i]) + (_Float16)1024.0f;
+            const f16x2 scale = {sv, sv}, bias = {zb, zb};
+            *reinterpret_cast<u32x4 *>(smem + buf + b_st[j] + i * THREADS * 64) =
+                dequant_word_natural(g.w[i][j], bias, scale);
+        }
+    };
+    auto store_all = [&](const Regs &g, uint32_t buf) {
+#pragma unroll
+        for (int p = 0; p < KSUB; ++p) store_part(g, buf, p);
+    };
+    // Fragments of MFMA substep ks: lane (row l % 32, k group l / 32) reads
+    // logical chunk 2*ks + l/32 of its row.
+    auto read_frag = [&](Frag &f, uint32_t buf, int ks) {
+        const uint32_t cofs = ((2 * ks + fkg) ^ fswz) * 16;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            f.a[i] = *reinterpret_cast<const f16x8 *>(smem + buf + fa + cofs + i * 32 * 128);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            f.b[j] = *reinterpret_cast<const f16x8 *>(smem + buf + fb + cofs + j * 32 * 128);
     };
 
     f32x16 acc[TM][TN];
@@ -139,32 +266,113 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int ktiles = (n_in + BK - 1) / BK;
-    load_tile(0);
-    for (int kt = 0; kt < ktiles; ++kt) {
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < ktiles) load_tile((kt + 1) * BK);
+    auto mma = [&](const Frag &f) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int kk = ks * 16 + 8 * (lane >> 5);
-            f16x8 af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const f16x8 *>(
-                    &As[(wave_m * WT_M + i * 32 + (lane & 31)) * LDK + kk]);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const f16x8 *>(
-                    &Bs[(wave_n * WT_N + j * 32 + (lane & 31)) * LDK + kk]);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+
+    constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
+    constexpr int VALU_PER_SUBSTEP = B_PART * 20;
+    constexpr int NVALU = (VALU_PER_SUBSTEP + NMFMA - 1) / NMFMA;
+
+    if (ksteps > 0) {
+        Regs R[3];
+        Frag f0, f1;
+        const int kmax = ksteps - 1;
+        load_all(R[0], 0);
+        load_all(R[1], min(1, kmax));
+        load_all(R[2], min(2, kmax));
+        store_all(R[0], 0);
+        load_all(R[0], min(3, kmax));
+        store_all(R[1], STAGE);
+        load_all(R[1], min(4, kmax));
+        __syncthreads();
+        read_frag(f0, 0, 0);
+
+        // Step k with k % 3 == J: MFMAs of step k from stage J (substep 0's
+        // fragments already in f0), step k+2's registers (set (J+2) % 3)
+        // into stage (J+2) % 3, that set reloaded with step k+5, and step
+        // k+1's first fragments read from stage (J+1) % 3.
+        auto step = [&](auto J_, int k) {
+            constexpr int J = decltype(J_)::value;
+            constexpr uint32_t cur = J * STAGE, nxt = ((J + 1) % 3) * STAGE, wr = ((J + 2) % 3) * STAGE;
+            Regs &g = R[(J + 2) % 3];
+            const int kl = min(k + 5, kmax);
+            read_frag(f1, cur, 1);
+            store_part(g, wr, 0);
+            load_a(g, kl, 0);
+            mma(f0);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART, NVALU>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(f0, cur, 2);
+            store_part(g, wr, 1);
+            load_a(g, kl, 1);
+            mma(f1);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART, NVALU>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(f1, cur, 3);
+            store_part(g, wr, 2);
+            load_a(g, kl, 2);
+            mma(f0);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART, NVALU>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(f0, nxt, 0);
+            store_part(g, wr, 3);
+            load_a(g, kl, 3);
+            load_b(g, kl);
+            mma(f1);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + 3 * B_SLICES, NVALU>();
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        int k = 0;
+        for (; k + 3 <= ksteps; k += 3) {
+            step(I0{}, k);
+            step(I1{}, k + 1);
+            step(I2{}, k + 2);
+        }
+        if (k < ksteps) step(I0{}, k);
+        if (k + 1 < ksteps) step(I1{}, k + 1);
+    }
+
+    if (n_in & (BK - 1)) {
+        // Final 32-wide step at k = 64 * ksteps: x chunks 0..3 and weight
+        // half 0 of every row, computed by substeps 0 and 1 only.  Every wave
+        // finished reading the real data of every stage before the last
+        // barrier, so stage 0 is free.
+        const int kt = ksteps;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < A_CHUNKS; ++i)
+            if ((tid & 7) < 4)
+                *reinterpret_cast<u32x4 *>(smem + a_st + i * THREADS * 16) =
+                    __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * (BK * 2), 0);
+        if (b_half == 0) {
+            const int gk = ((kt * BK) >> group_shift) * 2;
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < B_SLICES; ++i) {
+                const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK / 2), 0);
+                const _Float16 sv = bitcast<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(sr, soff[i], gk, 0));
+                const _Float16 zb = bitcast<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(zr, soff[i], gk, 0)) +
+                                    (_Float16)1024.0f;
+                const f16x2 scale = {sv, sv}, bias = {zb, zb};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<u32x4 *>(smem + b_st[j] + i * THREADS * 64) =
+                        dequant_word_natural(w[j], bias, scale);
+            }
         }
         __syncthreads();
+        Frag f;
+        read_frag(f, 0, 0);
+        mma(f);
+        read_frag(f, 0, 1);
+        mma(f);
     }
 
     // Lane l, register r of a 32x32 tile: column l % 32,
@@ -183,18 +391,40 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
         }
 }
 
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes)
+{
+    if (bytes <= 64 * 1024) return hipSuccess;
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    160 * 1024);
+    return e;
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                       const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
+                       uint16_t *y, hipStream_t stream)
+{
+    const int tiles_m = (m + BM - 1) / BM, tiles_n = (n_out + BN - 1) / BN;
+    const size_t lds = kStages * (size_t)(BM + BN) * 128;
+    auto kernel = gemm_kernel<BM, BN, WM, WN>;
+    const hipError_t e = allow_lds(kernel, lds);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
+    kernel<<<grid, block, lds, stream>>>(x, qweight, scales, zeros, y, m, n_out, n_in, group_shift,
+                                         tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
                           int group_size, uint16_t *y, hipStream_t stream)
 {
-    constexpr int BM = 128, BN = 128, BK = 64;
     int shift = 0;
     while ((1 << shift) < group_size) ++shift;
-    const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n_out + BN - 1) / BN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
-    gemm_kernel<BM, BN, BK, 2, 2><<<grid, block, 0, stream>>>(
-        x, qweight, scales, zeros, y, (int)m, (int)n_out, (int)n_in, shift, tiles_m, tiles_n);
-    return hipGetLastError();
+    return launch_gemm<256, 128, 2, 2>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
+                                          shift, y, stream);
 }
