@@ -271,7 +271,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
 
     constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
@@ -375,20 +375,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         mma(f);
     }
 
-    // Lane l, register r of a 32x32 tile: column l % 32,
-    // row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+    // The MFMAs take the weight fragment as their first operand, so tile
+    // (i, j) holds y^T: lane l, register r is output channel
+    // 8 * (r / 4) + 4 * (l / 32) + r % 4 of the tile's 32, for x row l % 32.
+    // The fp16 results go through LDS (row-major, rows padded to YS bytes,
+    // each lane writing its runs of 4 consecutive channels as 8 bytes), then
+    // every thread stores 16-byte pieces of whole rows, 16 lanes per 256
+    // bytes, so y is written in full cache lines.  The stages are free: every
+    // wave passed the last barrier (or the tail step's) after its last LDS
+    // read, and the barrier below orders the rest.
+    constexpr int YS = BN * 2 + 16;
+    static_assert(BM * YS <= kStages * STAGE, "output tile exceeds LDS");
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+        const int r = wave_m * WT_M + i * 32 + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wave_n * WT_N + j * 32 + (lane & 31);
-            if (col >= n_out) continue;
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wave_m * WT_M + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < m) y[(int64_t)row * n_out + col] = bitcast<uint16_t>((_Float16)acc[i][j][r]);
+            for (int rq = 0; rq < 4; ++rq) {
+                const int c = wave_n * WT_N + j * 32 + 8 * rq + 4 * (lane >> 5);
+                const f16x2 lo = {(_Float16)acc[i][j][4 * rq], (_Float16)acc[i][j][4 * rq + 1]};
+                const f16x2 hi = {(_Float16)acc[i][j][4 * rq + 2], (_Float16)acc[i][j][4 * rq + 3]};
+                const u32x2 v = {bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+                *reinterpret_cast<u32x2 *>(smem + r * YS + c * 2) = v;
             }
+    }
+    __syncthreads();
+    constexpr int CPR = BN / 8;                          // 16-byte pieces per row
+    constexpr int RPP = THREADS / CPR;                   // rows per pass
+    static_assert(CPR * RPP == THREADS && BM % RPP == 0, "output tile does not split evenly");
+    const bool vec16 = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && ((n_out & 7) == 0);
+    const int pc = tid % CPR, col = n0 + pc * 8;
+#pragma unroll 4
+    for (int r = tid / CPR; r < BM; r += RPP) {
+        const int row = m0 + r;
+        if (row >= m) break;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * YS + pc * 16);
+        uint16_t *yp = y + (int64_t)row * n_out + col;
+        if (vec16 && col + 8 <= n_out) {
+            *reinterpret_cast<u32x4 *>(yp) = v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (col + e < n_out) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
         }
+    }
 }
 
 template <typename K>
@@ -425,6 +457,6 @@ hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint
 {
     int shift = 0;
     while ((1 << shift) < group_size) ++shift;
-    return launch_gemm<256, 128, 2, 2>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
+    return launch_gemm<256, 128, 4, 1>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
                                           shift, y, stream);
 }
