@@ -307,6 +307,11 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the timed decode graph (no extras, no per-linear reference, no CPU leg); "
                          "used for profiling")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill GEMM phase, printed as its own JSON line; used for profiling")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one elementwise copy of 256 MiB (268435456 bytes read and written), "
+                         "the known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
 
@@ -321,6 +326,25 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
 
+    if args.copy_calibration:
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        log("copy calibration: torch.neg over 268435456 bytes (read) into 268435456 bytes (written)")
+        del a, b
+    if args.prefill_only:
+        pre = bench_prefill(args, dev)
+        log(f"prefill: {pre}")
+        print(json.dumps({
+            "metric": "W4A16 prefill GEMM TFLOP/s (m=2048)", "value": pre["tflops"], "unit": "TFLOP/s",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+            "data": "synthetic", "config": {"workload": "prefill m=2048 on the 7B linear shapes"},
+            "prefill": pre, "roofline": {"bound": "mfma", "achieved": pre["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4)}}),
+              flush=True)
+        return
     if args.decode_only:
         args.no_extras = True
         args.no_cpu_baseline = True
