@@ -276,9 +276,10 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
 
     // ---- staging of x (chunk c = (row, block, quarter) holds 32 values) and
     // of the scale|zero pairs of rows row0 .. row0 + ROWS.  The first batch
-    // of staging loads is issued before the first DEPTH-1 weight stages, so
-    // the LDS stores below wait only for the (cache-hot) staging data while
-    // the weights stay in flight across the barrier.
+    // of staging loads is issued before the first DEPTH weight stages (the
+    // whole ring), so the LDS stores below wait only for the staging data
+    // while every ring stage stays in flight across the barrier; a wave with
+    // at most DEPTH stages has all its weights requested before it.
     const int nstages = (kblocks + SB - 1) / SB;
     const int n_chunks = m * kblocks * 4;
     const int n_items = ROWS * G;
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     sz_load(tid, s8, z8);
     Stage<CT, UNROLL> ring[DEPTH];
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) load_stage(ring[d], d);
+    for (int d = 0; d < DEPTH; ++d) load_stage(ring[d], d);
     x_store(tid, xv);
     sz_store(tid, s8, z8);
     for (int c = tid + THREADS; c < n_chunks; c += THREADS) {
@@ -376,13 +377,14 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
         }
     };
 
-    // ---- stream the weights through the register ring ----
+    // ---- stream the weights through the register ring: each slot is
+    // refilled with the stage DEPTH ahead as soon as it has been consumed ----
     for (int i0 = 0; i0 < nstages; i0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int i = i0 + d;
-            load_stage(ring[(d + DEPTH - 1) % DEPTH], i + DEPTH - 1);
             if (i < nstages) compute(ring[d], i);
+            load_stage(ring[d], i + DEPTH);
         }
     }
     if (SPLIT > 1) __syncthreads();           // the partial sums reuse the x buffer
@@ -641,14 +643,20 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
     if (plan_window<S, C, U, FOLD, MM>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
     if (kblocks >= 16) {
         if (!FOLD) {
+            if (m == 1) {
+                if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 1, 3);
+                if (kblocks >= 128 && tiles >= 512) Q4_RES(16, 1, 1, 2);
+                if (tiles <= 768) Q4_RES(8, 1, 1, 2);
+                Q4_RES(4, 2, 1, 2);
+            }
             Q4_RES(16, 1, 1, 4);
         } else if (m == 1) {
-            if (tiles <= 256) Q4_RES(16, 1, 1, 2);
+            if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 1, 3);
             if (kblocks >= 128 && tiles >= 512) Q4_RES(8, 2, 1, 2);
             if (tiles <= 768) Q4_RES(8, 1, 1, 2);
-            Q4_RES(4, 2, 1, 4);
+            Q4_RES(4, 2, 1, 2);
         } else {
-            if (tiles >= 640) Q4_RES(16, 4, 1, 2);
+            if (tiles >= 640) Q4_RES(8, 4, 1, 2);
             if (tiles >= 256) Q4_RES(8, 2, 1, 2);
             Q4_RES(8, 1, 1, 2);
         }
