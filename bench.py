@@ -262,6 +262,28 @@ def student_t_device(n_out, n_in, seed, dev):
     return z.mul_(torch.rsqrt(chi2.div_(3.0))).mul_(0.02)
 
 
+def bench_single(args, dev):
+    """One 4096x4096 linear at m=1 (g=128), cycled over 64 distinct packed copies
+    (about 570 MB, beyond the 256 MB Infinity Cache) inside one graph: the
+    latency-dominated single-GEMV case."""
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    n_out = n_in = 4096
+    w = syn.normal_weight_device(n_out, n_in, 1, 0.02, 8, dev)
+    qws = [w4.quantize_pack(w.mul(1.0 + c * 1e-3) if c else w, 128) for c in range(64)]
+    del w
+    x = syn.activations_f16_device(1, n_in, 101, dev)
+    y = torch.empty((1, n_out), dtype=torch.float16, device=dev)
+    gr = capture(lambda: [w4.gemv(x, q, y) for q in qws])
+    el, _ = time_graph(gr, 3, 1)
+    t = el / (3 * len(qws))
+    del qws, gr
+    torch.cuda.empty_cache()
+    return dict(us_per_launch=round(t * 1e6, 2),
+                gbs=round(algorithmic_bytes(n_out, n_in, 1, 128) / t / 1e9, 1))
+
+
 def bench_stress_and_quantize(args, dev):
     import torch
     import w4a16_dequant_gemv_amd as w4
@@ -359,6 +381,8 @@ def main():
         log(f"decode70b: {extras['decode70b']}")
         extras["stress"] = bench_stress_and_quantize(args, dev)
         log(f"stress: {extras['stress']}")
+        extras["single"] = bench_single(args, dev)
+        log(f"single 4096x4096 GEMV: {extras['single']}")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host_w, args.cpu_seconds)
@@ -400,6 +424,7 @@ def main():
             "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
         record["decode70b"] = dict(extras["decode70b"], frac=round(extras["decode70b"]["gbs"] / HBM_PEAK_GBS, 4))
         record["stress"] = extras["stress"]
+        record["single_gemv_4096x4096"] = extras["single"]
     print(json.dumps(record), flush=True)
 
 
