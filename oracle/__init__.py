@@ -1,4 +1,5 @@
-"""CPU oracle for group-wise INT4 quantization and the W4A16 linear layer.
+"""CPU oracle for group-wise (or per-channel) INT4 / INT8 weight quantization
+and the W4A16 / W8A16 linear layer.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The GPU library
@@ -43,6 +44,10 @@ class Oracle:
         lib.orc_quantize_pack.argtypes = [_p, _c_i64, _c_i64, _c_i32, _c_i32,
                                           _p, _p, _p, _p]
         lib.orc_dequant.argtypes = [_p, _p, _p, _c_i64, _c_i64, _c_i32, _p]
+        lib.orc_quantize_pack_bits.restype = ctypes.c_int
+        lib.orc_quantize_pack_bits.argtypes = [_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                               _p, _p, _p, _p]
+        lib.orc_dequant_bits.argtypes = [_p, _p, _p, _c_i64, _c_i64, _c_i32, _c_i32, _p]
         lib.orc_linear_ref.argtypes = [_p, _p, _c_i64, _c_i64, _c_i64, _p, _p]
         self.lib = lib
 
@@ -75,34 +80,45 @@ class Oracle:
                                     s.ctypes.data, z.ctypes.data, q.ctypes.data)
         return s[0], int(z[0]), q
 
-    def quantize_pack(self, w, group_size=128, symmetric=False):
-        """W fp32 [n_out][n_in] -> (packed u32 [n_out][n_in/8], scales fp16 bits,
-        zeros fp16 bits [n_out][n_in/g], fp32 scales before storage)."""
+    def quantize_pack(self, w, group_size=128, symmetric=False, bits=4):
+        """W fp32 [n_out][n_in] -> (packed u32 [n_out][n_in*bits/32], scales fp16
+        bits, zeros fp16 bits [n_out][n_in/g], fp32 scales before storage).
+        bits is 4 or 8; group_size == n_in is per-channel."""
         w = np.ascontiguousarray(w, dtype=np.float32)
         n_out, n_in = w.shape
         g = n_in // group_size
-        packed = np.empty((n_out, n_in // 8), dtype=np.uint32)
+        packed = np.empty((n_out, n_in * bits // 32), dtype=np.uint32)
         scales = np.empty((n_out, g), dtype=np.uint16)
         zeros = np.empty((n_out, g), dtype=np.uint16)
         s32 = np.empty((n_out, g), dtype=np.float32)
-        rc = self.lib.orc_quantize_pack(w.ctypes.data, n_out, n_in, group_size,
-                                        int(bool(symmetric)), packed.ctypes.data,
-                                        scales.ctypes.data, zeros.ctypes.data,
-                                        s32.ctypes.data)
+        if bits == 4:
+            rc = self.lib.orc_quantize_pack(w.ctypes.data, n_out, n_in, group_size,
+                                            int(bool(symmetric)), packed.ctypes.data,
+                                            scales.ctypes.data, zeros.ctypes.data,
+                                            s32.ctypes.data)
+        else:
+            rc = self.lib.orc_quantize_pack_bits(w.ctypes.data, n_out, n_in, group_size, bits,
+                                                 int(bool(symmetric)), packed.ctypes.data,
+                                                 scales.ctypes.data, zeros.ctypes.data,
+                                                 s32.ctypes.data)
         if rc != 0:
-            raise ValueError(f"oracle rejected shape {w.shape} with group_size {group_size}")
+            raise ValueError(f"oracle rejected shape {w.shape} with group_size {group_size}, bits {bits}")
         return packed, scales, zeros, s32
 
-    def dequant(self, packed, scales, zeros, group_size):
+    def dequant(self, packed, scales, zeros, group_size, bits=4):
         """-> w' fp32 [n_out][n_in], w' = s * (q - z)."""
         packed = np.ascontiguousarray(packed, dtype=np.uint32)
         scales = np.ascontiguousarray(scales, dtype=np.uint16)
         zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
         n_out, words = packed.shape
-        n_in = words * 8
+        n_in = words * (32 // bits)
         out = np.empty((n_out, n_in), dtype=np.float32)
-        self.lib.orc_dequant(packed.ctypes.data, scales.ctypes.data, zeros.ctypes.data,
-                             n_out, n_in, group_size, out.ctypes.data)
+        if bits == 4:
+            self.lib.orc_dequant(packed.ctypes.data, scales.ctypes.data, zeros.ctypes.data,
+                                 n_out, n_in, group_size, out.ctypes.data)
+        else:
+            self.lib.orc_dequant_bits(packed.ctypes.data, scales.ctypes.data, zeros.ctypes.data,
+                                      n_out, n_in, group_size, bits, out.ctypes.data)
         return out
 
     def linear_ref(self, x_f16_bits, w_deq):
@@ -119,9 +135,9 @@ class Oracle:
                                 y.ctypes.data, a.ctypes.data)
         return y, a
 
-    def linear_from_packed(self, x_f16_bits, packed, scales, zeros, group_size):
+    def linear_from_packed(self, x_f16_bits, packed, scales, zeros, group_size, bits=4):
         """Dequantize, then take the reference product (two plain steps)."""
-        return self.linear_ref(x_f16_bits, self.dequant(packed, scales, zeros, group_size))
+        return self.linear_ref(x_f16_bits, self.dequant(packed, scales, zeros, group_size, bits))
 
 
 _DEFAULT = None

@@ -1,6 +1,6 @@
 /*
- * q4_oracle.c -- CPU oracle for group-wise INT4 weight quantization and the
- * W4A16 linear layer.
+ * q4_oracle.c -- CPU oracle for group-wise INT4 / INT8 weight quantization
+ * (per group or per output channel) and the W4A16 / W8A16 linear layer.
  *
  * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct
  * definition that the GPU library is checked against.  Only the tests, the
@@ -27,15 +27,19 @@
  *   - z is clipped to [0, 2^b - 1] as in [Path] §2.1;
  *   - codes are computed from the fp32 s; fp16 is the storage type of s, z;
  *   - rounding is round-half-to-even (torch.round / np.round semantics);
- *   - symmetric 4-bit codes q in [-8, 7] are stored offset-binary as q + 8
- *     with a stored zero-point of 8, so dequantization is mode-agnostic;
- *   - packing (not on the pages): element 8j+t of a row sits in bits
- *     4t..4t+3 of 32-bit word j of that row, rows are [n_out][n_in/8].
+ *   - symmetric b-bit codes q in [-2^(b-1), 2^(b-1) - 1] are stored
+ *     offset-binary as q + 2^(b-1) with a stored zero-point of 2^(b-1), so
+ *     dequantization is mode-agnostic;
+ *   - packing (not on the pages): element (32/b) j + t of a row sits in bits
+ *     b t .. b t + b - 1 of 32-bit word j of that row, rows are
+ *     [n_out][n_in * b / 32];
+ *   - per-channel quantization is the group size n_in (one group per row).
  *
  * Parity status of each function is stated beside it.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------------ */
@@ -183,70 +187,107 @@ void orc_quantize_group(const float *v, int64_t n, int bits, int symmetric,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Per-group INT4 quantization of W[n_out][n_in] along the input dimension,  */
-/* fp16 storage of s and z, and packing of 8 codes per 32-bit word.          */
-/* [Guide] §2.2 (W[out_features, in_features], one scale per group of 128    */
-/* input elements per output channel, fp16 scale); [Zero] §3.1 (each block   */
-/* keeps its own S and Z); [Path] §2.2 (group_size 128 / 64).                */
-/* The packing order is this library's convention; it is pinned only by the  */
+/* Per-group b-bit quantization (b = 4 or 8) of W[n_out][n_in] along the     */
+/* input dimension, fp16 storage of s and z, and packing of 32/b codes per   */
+/* 32-bit word.                                                              */
+/* [Guide] §2.2 (W[out_features, in_features]; one scale per group of 128    */
+/* input elements per output channel for INT4, one scale per output channel */
+/* -- per-channel -- for INT8 weights; fp16 scale); [Guide] §2.3 (W8A16:     */
+/* INT8 weights, FP16 activations); [Guide] §2.1 and [Path] §2.1 (the b-bit  */
+/* code ranges); [Zero] §3.1 (each block keeps its own S and Z); [Path] §2.2 */
+/* (group_size 128 / 64).  group_size may be any divisor of n_in;           */
+/* group_size == n_in is the per-channel case.  Symmetric codes q are        */
+/* stored offset-binary as q + 2^(b-1) with a stored zero-point of 2^(b-1).  */
+/* The packing order is this library's convention (element k of a row in    */
+/* bits b*(k % (32/b)) .. of word k / (32/b)); it is pinned only by the      */
 /* brute-force unpack (parity unpinned against the pages, which give none).  */
+/* Returns 0, 1 for an unsupported shape, 2 if scratch memory ran out.       */
 /* ------------------------------------------------------------------------ */
-int orc_quantize_pack(const float *w, int64_t n_out, int64_t n_in,
-                      int32_t group_size, int32_t symmetric,
-                      uint32_t *packed, uint16_t *scales, uint16_t *zeros,
-                      float *s_fp32 /* may be NULL */)
+int orc_quantize_pack_bits(const float *w, int64_t n_out, int64_t n_in,
+                           int32_t group_size, int32_t bits, int32_t symmetric,
+                           uint32_t *packed, uint16_t *scales, uint16_t *zeros,
+                           float *s_fp32 /* may be NULL */)
 {
-    if (group_size <= 0 || group_size > 1024 || n_in % group_size != 0 ||
-        n_in % 8 != 0)
+    if ((bits != 4 && bits != 8) || group_size <= 0 || n_in % group_size != 0 ||
+        n_in % (32 / bits) != 0)
         return 1;
+    const int per_word = 32 / bits;
+    const int64_t words = n_in / per_word;
     const int64_t groups = n_in / group_size;
+    const int32_t offset = 1 << (bits - 1);
+    int failed = 0;
 
     #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < n_out; n++) {
-        int32_t codes[1024];
-        uint32_t *row = packed + n * (n_in / 8);
-        memset(row, 0, (size_t)(n_in / 8) * sizeof(uint32_t));
+        int32_t *codes = (int32_t *)malloc((size_t)group_size * sizeof(int32_t));
+        if (!codes) {
+            #pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        uint32_t *row = packed + n * words;
+        memset(row, 0, (size_t)words * sizeof(uint32_t));
         for (int64_t j = 0; j < groups; j++) {
             const float *v = w + n * n_in + j * group_size;
             float s;
             int32_t z;
-            orc_quantize_group(v, group_size, 4, symmetric, &s, &z, codes);
-            int32_t z_store = symmetric ? 8 : z;
+            orc_quantize_group(v, group_size, bits, symmetric, &s, &z, codes);
+            int32_t z_store = symmetric ? offset : z;
             for (int64_t t = 0; t < group_size; t++) {
-                uint32_t u = (uint32_t)(symmetric ? codes[t] + 8 : codes[t]);
+                uint32_t u = (uint32_t)(symmetric ? codes[t] + offset : codes[t]);
                 int64_t k = j * group_size + t;
-                row[k / 8] |= u << (4 * (k % 8));
+                row[k / per_word] |= u << (bits * (k % per_word));
             }
             scales[n * groups + j] = orc_f32_to_f16(s);
             zeros[n * groups + j] = orc_f32_to_f16((float)z_store);
             if (s_fp32)
                 s_fp32[n * groups + j] = s;
         }
+        free(codes);
     }
-    return 0;
+    return failed ? 2 : 0;
+}
+
+/* The INT4 case: 8 codes per word, [n_out][n_in/8]. */
+int orc_quantize_pack(const float *w, int64_t n_out, int64_t n_in,
+                      int32_t group_size, int32_t symmetric,
+                      uint32_t *packed, uint16_t *scales, uint16_t *zeros,
+                      float *s_fp32 /* may be NULL */)
+{
+    return orc_quantize_pack_bits(w, n_out, n_in, group_size, 4, symmetric, packed,
+                                  scales, zeros, s_fp32);
 }
 
 /* ------------------------------------------------------------------------ */
 /* Dequantization w' = s * (q - z) in float32.                               */
 /* [Guide] §2.1 (x_hat = s * (q - z); dequantize_tensor returns float32);    */
 /* [Zero] §2 (f' = S * (q - Z)).  The product of an fp16 scale and an        */
-/* integer in [-15, 15] is exact in binary32.                                */
+/* integer in [-255, 255] is exact in binary32.                              */
 /* ------------------------------------------------------------------------ */
-void orc_dequant(const uint32_t *packed, const uint16_t *scales,
-                 const uint16_t *zeros, int64_t n_out, int64_t n_in,
-                 int32_t group_size, float *out)
+void orc_dequant_bits(const uint32_t *packed, const uint16_t *scales,
+                      const uint16_t *zeros, int64_t n_out, int64_t n_in,
+                      int32_t group_size, int32_t bits, float *out)
 {
+    const int per_word = 32 / bits;
+    const uint32_t mask = (1u << bits) - 1u;
     const int64_t groups = n_in / group_size;
     #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < n_out; n++) {
         for (int64_t k = 0; k < n_in; k++) {
-            uint32_t word = packed[n * (n_in / 8) + k / 8];
-            int32_t u = (int32_t)((word >> (4 * (k % 8))) & 0xFu);
+            uint32_t word = packed[n * (n_in / per_word) + k / per_word];
+            int32_t u = (int32_t)((word >> (bits * (k % per_word))) & mask);
             float s = orc_f16_to_f32(scales[n * groups + k / group_size]);
             int32_t z = (int32_t)orc_f16_to_f32(zeros[n * groups + k / group_size]);
             out[n * n_in + k] = s * (float)(u - z);
         }
     }
+}
+
+void orc_dequant(const uint32_t *packed, const uint16_t *scales,
+                 const uint16_t *zeros, int64_t n_out, int64_t n_in,
+                 int32_t group_size, float *out)
+{
+    orc_dequant_bits(packed, scales, zeros, n_out, n_in, group_size, 4, out);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -351,8 +351,110 @@ def pin_linear_ref(orc, quick=False):
     assert np.all(y0 == 0) and np.all(a0 == 0)
 
 
+# ---------------------------------------------------------------------------
+# INT8 codes (W8A16) and per-channel groups ([Guide] §2.1 b-bit ranges,
+# §2.2 per-channel for INT8 weights, §2.3 W8A16).
+# ---------------------------------------------------------------------------
+def _codes_b(packed, bits):
+    per = 32 // bits
+    shifts = (bits * np.arange(per, dtype=np.uint32))
+    return ((packed[..., None] >> shifts) & ((1 << bits) - 1)).reshape(packed.shape[0], -1)
+
+
+def pin_brute_force_int8_per_channel(orc, quick=False):
+    cases = _small_cases()[:1] if quick else _small_cases()
+    for ci, w in enumerate(cases):
+        n_in = w.shape[1]
+        for bits, g in ((8, 32), (8, n_in), (4, n_in)):
+            for sym in (False, True):
+                packed, scales, zeros, s32 = orc.quantize_pack(w, g, sym, bits=bits)
+                assert packed.shape == (w.shape[0], n_in * bits // 32)
+                assert scales.shape == (w.shape[0], n_in // g)
+                try:
+                    check_matrix(w, packed, scales, zeros, s32, g, sym, bits=bits)
+                except AssertionError as e:
+                    raise AssertionError(f"case {ci} bits={bits} g={g} sym={sym}: {e}") from None
+
+
+def pin_ties_to_even_int8(orc, quick=False):
+    # asymmetric: range [-127, 128] gives s = 255/255 = 1 exactly and z = 127
+    vals = [-127.0, 128.0, 0.5, 1.5, 2.5, -0.5, -1.5, 3.5, -2.5, 100.5, -99.5] + [0.0] * 21
+    w = np.array([vals], dtype=np.float32)
+    for g in (32, 32):                               # one group == the whole row (per-channel)
+        packed, scales, zeros, s32 = orc.quantize_pack(w, g, False, bits=8)
+        assert float(s32[0, 0]) == 1.0 and float(_f16_bits_to_f32(zeros)[0, 0]) == 127.0
+        codes = _codes_b(packed, 8)[0].tolist()
+        want = [round(v) + 127 for v in vals]        # Python's round: half to even
+        assert codes == want, f"int8 tie codes {codes[:11]} != {want[:11]}"
+    # symmetric: max|w| = 127 gives s = 1; codes stored as q + 128
+    vals_s = [127.0, -126.5, 0.5, 1.5, 2.5, -0.5, -3.5, 5.5, -127.0, 126.5] + [0.0] * 22
+    w = np.array([vals_s], dtype=np.float32)
+    packed, scales, zeros, s32 = orc.quantize_pack(w, 32, True, bits=8)
+    assert float(s32[0, 0]) == 1.0 and float(_f16_bits_to_f32(zeros)[0, 0]) == 128.0
+    codes = _codes_b(packed, 8)[0].tolist()
+    assert codes == [round(v) + 128 for v in vals_s], f"int8 symmetric tie codes {codes[:10]}"
+
+
+def pin_grid_exact_int8(orc, quick=False):
+    rng = np.random.default_rng(42)
+    rows, n_in = 12, 512
+    w = np.empty((rows, n_in), dtype=np.float32)
+    expect = []
+    for r in range(rows):
+        s = np.float32(np.float16(rng.uniform(1e-4, 0.02)))          # fp16-exact scale
+        z = int(rng.integers(0, 256))
+        u = rng.integers(0, 256, size=n_in)
+        u[rng.integers(0, n_in)] = 0
+        u[rng.integers(0, n_in)] = 255
+        w[r] = s * (u - z).astype(np.float32)                        # exact in binary32
+        expect.append((s, z, u))
+    packed, scales, zeros, s32 = orc.quantize_pack(w, n_in, False, bits=8)   # per-channel
+    codes = _codes_b(packed, 8)
+    sh, zh = _f16_bits_to_f32(scales), _f16_bits_to_f32(zeros)
+    for r, (s, z, u) in enumerate(expect):
+        assert sh[r, 0] == s and zh[r, 0] == z, f"row {r}: (s, z) = ({sh[r, 0]}, {zh[r, 0]}) != ({s}, {z})"
+        assert np.array_equal(codes[r], u), f"row {r}: int8 codes differ"
+    wd = orc.dequant(packed, scales, zeros, n_in, bits=8)
+    assert np.array_equal(wd.view(np.uint32), w.view(np.uint32)), "grid-exact int8 W not reproduced bitwise"
+
+
+def pin_dequant_int8(orc, quick=False):
+    rng = np.random.default_rng(72)
+    n_out, n_in = 20, 384
+    for g in (64, n_in):
+        packed = rng.integers(0, 1 << 32, size=(n_out, n_in // 4), dtype=np.uint64).astype(np.uint32)
+        s = rng.uniform(0, 0.01, size=(n_out, n_in // g)).astype(np.float16)
+        s[0, 0] = 0.0
+        s[1, 0] = np.float16(6e-8)                    # fp16 subnormal
+        z = rng.integers(0, 256, size=(n_out, n_in // g)).astype(np.float16)
+        got = orc.dequant(packed, s.view(np.uint16), z.view(np.uint16), g, bits=8)
+        bytes_ = packed.view(np.uint8).reshape(n_out, n_in).astype(np.int64)   # little-endian bytes
+        want = (s.astype(np.float32).repeat(g, axis=1)
+                * (bytes_ - z.astype(np.int64).repeat(g, axis=1)).astype(np.float32))
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"int8 dequant g={g} differs bitwise"
+
+
+def pin_reconstruction_bound_int8(orc, quick=False):
+    rows = 16 if quick else 64
+    w = synthetic.normal_weight(rows, 4096, seed=33, std=0.02, n_outlier_cols=8)
+    for bits, g in ((8, 4096), (8, 128), (4, 4096)):
+        for sym in (False, True):
+            packed, scales, zeros, s32 = orc.quantize_pack(w, g, sym, bits=bits)
+            wd = orc.dequant(packed, scales, zeros, g, bits=bits)
+            s = s32.astype(np.float64).repeat(g, axis=1)
+            sh = _f16_bits_to_f32(scales).astype(np.float64).repeat(g, axis=1)
+            cmax = (1 << (bits - 1)) if sym else (1 << bits) - 1
+            err = np.abs(w.astype(np.float64) - wd.astype(np.float64))
+            bound = s * (0.5 + 2.0 ** -18) + cmax * np.abs(s - sh)
+            bad = err > bound
+            assert not bad.any(), (f"bits={bits} g={g} sym={sym}: |w-w'| exceeds s/2 at "
+                                   f"{np.argwhere(bad)[:3].tolist()}")
+
+
 ALL_PINS = [
     pin_worked_example, pin_brute_force, pin_ties_to_even, pin_zero_clip,
     pin_reconstruction_bound, pin_idempotence, pin_grid_exact, pin_constant_groups,
     pin_storage_accounting, pin_f16_converter, pin_dequant, pin_linear_ref,
+    pin_brute_force_int8_per_channel, pin_ties_to_even_int8, pin_grid_exact_int8,
+    pin_dequant_int8, pin_reconstruction_bound_int8,
 ]

@@ -22,16 +22,22 @@ MUTANTS = {
     "asym_divisor_2b": ("float s = (mx - mn) / qmax;", "float s = (mx - mn) / (qmax + 1.0f);"),
     "sym_divisor_2b_minus_1": ("const float qmax = (float)((1 << (bits - 1)) - 1);",
                                "const float qmax = (float)((1 << bits) - 1);"),
-    "sym_offset_7": ("codes[t] + 8 : codes[t]", "codes[t] + 7 : codes[t]"),
-    "nibble_order_reversed": ("row[k / 8] |= u << (4 * (k % 8));",
-                              "row[k / 8] |= u << (4 * (7 - k % 8));"),
+    "sym_offset_7": ("codes[t] + offset : codes[t]", "codes[t] + offset - 1 : codes[t]"),
+    "sym_offset_fixed_8": ("const int32_t offset = 1 << (bits - 1);", "const int32_t offset = 8;"),
+    "nibble_order_reversed": ("row[k / per_word] |= u << (bits * (k % per_word));",
+                              "row[k / per_word] |= u << (bits * (per_word - 1 - k % per_word));"),
+    "pack_shift_4": ("row[k / per_word] |= u << (bits * (k % per_word));",
+                     "row[k / per_word] |= u << (4 * (k % per_word));"),
+    "group_capped_1024": ("orc_quantize_group(v, group_size, bits, symmetric, &s, &z, codes);",
+                          "orc_quantize_group(v, group_size > 1024 ? 1024 : group_size, bits, symmetric, &s, &z, codes);"),
     "min_init_zero": ("float mn = v[0], mx = v[0];", "float mn = 0.0f, mx = v[0];"),
     "dequant_sign": ("out[n * n_in + k] = s * (float)(u - z);",
                      "out[n * n_in + k] = s * (float)(z - u);"),
     "dequant_group_index": ("float s = orc_f16_to_f32(scales[n * groups + k / group_size]);",
                             "float s = orc_f16_to_f32(scales[n * groups + (k / group_size + 1) % groups]);"),
-    "dequant_nibble_index": ("int32_t u = (int32_t)((word >> (4 * (k % 8))) & 0xFu);",
-                             "int32_t u = (int32_t)((word >> (4 * ((k + 1) % 8))) & 0xFu);"),
+    "dequant_nibble_index": ("int32_t u = (int32_t)((word >> (bits * (k % per_word))) & mask);",
+                             "int32_t u = (int32_t)((word >> (bits * ((k + 1) % per_word))) & mask);"),
+    "dequant_mask_4bit": ("const uint32_t mask = (1u << bits) - 1u;", "const uint32_t mask = 0xFu;"),
     "f16_truncate": ("if (rem > half || (rem == half && (q & 1u)))", "if (0)"),
     "f16_ties_away": ("if (rem > half || (rem == half && (q & 1u)))", "if (rem >= half)"),
     "f16_subnormal_scale": ("float mag = (float)frac * 0x1p-24f;", "float mag = (float)frac * 0x1p-23f;"),
