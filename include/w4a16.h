@@ -1,8 +1,10 @@
 /*
  * w4a16.h -- C ABI of the W4A16 library for AMD Instinct MI355X (gfx950):
- * group-wise INT4 weight quantization with packing, dequantization, and the
- * linear layer y = x W'^T that unpacks and dequantizes the weights on the fly
- * (decode GEMV for 1..16 rows of x, prefill GEMM for any number of rows).
+ * group-wise (or per-channel) INT4 weight quantization with packing,
+ * dequantization, and the linear layer y = x W'^T that unpacks and
+ * dequantizes the weights on the fly (decode GEMV for 1..16 rows of x,
+ * prefill GEMM for any number of rows); the same for INT8 weights (W8A16,
+ * the q8_* entry points).
  *
  * Sources (cited by page title and section):
  *   [Guide] "27届大模型面试准备十九 模型量化全攻略 -- INT8/INT4、GPTQ、AWQ、
@@ -20,18 +22,24 @@
  *  - Layouts are dense row-major.  W and W' are [n_out][n_in] ([Guide] §2.2
  *    takes W as [out_features, in_features]); groups run along n_in.
  *  - fp16 values travel as uint16_t bit patterns (IEEE binary16).
- *  - Packed weights: uint32_t [n_out][n_in / 8]; element k of a row is the
- *    4-bit code in bits 4*(k % 8) .. 4*(k % 8) + 3 of word k / 8.
+ *  - Packed weights, q4_*: uint32_t [n_out][n_in / 8]; element k of a row is
+ *    the 4-bit code in bits 4*(k % 8) .. 4*(k % 8) + 3 of word k / 8.
+ *    q8_*: uint32_t [n_out][n_in / 4]; element k is the byte in bits
+ *    8*(k % 4) .. 8*(k % 4) + 7 of word k / 4.
  *  - Scales and zero-points: fp16 [n_out][n_in / group_size].  Symmetric
- *    quantization stores its signed codes q in [-8, 7] as q + 8 with a stored
- *    zero-point of 8, so every consumer computes w' = s * (code - z).
+ *    quantization stores its signed b-bit codes q in [-2^(b-1), 2^(b-1) - 1]
+ *    as q + 2^(b-1) with a stored zero-point of 2^(b-1) (8 for INT4, 128 for
+ *    INT8), so every consumer computes w' = s * (code - z).
  *  - Outputs are fully overwritten; inputs must not overlap outputs.
  *  - Return value: Q4_OK, or one of the Q4_ERR_* codes below.  Argument
  *    errors are detected before any HIP call is made.  A fault inside a
  *    kernel surfaces at the caller's next synchronization, not here.
  *  - Supported group sizes are 32, 64, 128 and 256 ([Zero] §3.1 names
- *    blocks of 32 and 256, [Path] §2.2 groups of 128 and 64).  Any other size
- *    is rejected with Q4_ERR_GROUP rather than served by a slow generic path.
+ *    blocks of 32 and 256, [Path] §2.2 groups of 128 and 64), and
+ *    group_size == n_in: one scale and zero-point per output channel
+ *    ([Guide] §2.2, the usual granularity for INT8 weights), for any n_in
+ *    that is a multiple of 32.  Any other size is rejected with
+ *    Q4_ERR_GROUP rather than served by a slow generic path.
  *  - Inputs containing NaN or Inf give unspecified (but memory-safe) results.
  *  - Calls are thread-safe; the library keeps no mutable global state.
  */
@@ -44,14 +52,15 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 1
+#define Q4_ABI_VERSION 2
 
 enum {
     Q4_OK = 0,
     Q4_ERR_NULL = 1,   /* a required pointer is NULL */
     Q4_ERR_SHAPE = 2,  /* a size <= 0 or too large, n_in % group_size != 0,
                           or m outside the entry point's range */
-    Q4_ERR_GROUP = 3,  /* group_size not in {32, 64, 128, 256} */
+    Q4_ERR_GROUP = 3,  /* group_size not in {32, 64, 128, 256} and not
+                          n_in (per-channel with n_in a multiple of 32) */
     Q4_ERR_ALIGN = 4,  /* w, w_out, qweight or x not 16-byte aligned, or an
                           fp16 array not 2-byte aligned */
     Q4_ERR_HIP = 5     /* the HIP runtime refused the launch; see
@@ -59,7 +68,7 @@ enum {
 };
 
 /* Largest sizes accepted: n_in <= 2^20, n_out <= 2^24, m <= 2^24, and
- * n_out * n_in <= 2^36 elements. */
+ * n_out * n_in, m * n_in and m * n_out each <= 2^34 elements. */
 
 /* Q4_ABI_VERSION of the loaded library. */
 int q4_abi_version(void);
@@ -124,6 +133,34 @@ int q4_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
 int q4_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
             const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
             int32_t group_size, uint16_t *y, void *stream);
+
+/*
+ * INT8 weights (W8A16, [Guide] §2.3: INT8 weights, FP16 activations).
+ * Group-wise or per-channel INT8 quantization and packing of W (fp32
+ * [n_out][n_in]), the 8-bit case of the same affine map ([Guide] §2.1:
+ * asymmetric s = (max - min)/(2^b - 1), symmetric s = max|x|/(2^(b-1) - 1);
+ * [Path] §2.1 clips z and the codes), all in binary32 with RNE:
+ *   asymmetric: s = max((max - min) / 255, 1e-8), z = clamp(rint(-min/s), 0, 255),
+ *               code = clamp(rint(w/s) + z, 0, 255);
+ *   symmetric:  s = max(max|w| / 127, 1e-8), q = clamp(rint(w/s), -128, 127),
+ *               code = q + 128, stored zero-point 128.
+ * Writes qweight (u32 [n_out][n_in/4]), scales and zeros (fp16
+ * [n_out][n_in/group_size]), bit-exact.  group_size == n_in gives one scale
+ * per output channel.  Same alignment rules as q4_quantize_pack.
+ */
+int q8_quantize_pack(const float *w, int64_t n_out, int64_t n_in,
+                     int32_t group_size, int32_t symmetric,
+                     uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                     void *stream);
+
+/*
+ * INT8 dequantization w' = s * (code - z) into fp32 w_out [n_out][n_in];
+ * the product of an fp16 scale and an integer in [-255, 255] is exact in
+ * binary32, so the result is bit-exact.  Same alignment rules as q4_dequant.
+ */
+int q8_dequant(const uint32_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+               int64_t n_out, int64_t n_in, int32_t group_size, float *w_out,
+               void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,14 +25,14 @@ def u32_bits(t):
     return t.detach().cpu().contiguous().numpy().view(np.uint32)
 
 
-def qweight_from_oracle(packed, scales, zeros, group_size, symmetric=False):
+def qweight_from_oracle(packed, scales, zeros, group_size, symmetric=False, bits=4):
     """Oracle-produced packed weights as a QuantizedWeight on the GPU."""
     from w4a16_dequant_gemv_amd.api import QuantizedWeight
     n_out, words = packed.shape
     return QuantizedWeight(to_dev(packed.view(np.int32)),
                            to_dev(scales).view(torch.float16),
                            to_dev(zeros).view(torch.float16),
-                           n_out, words * 8, group_size, symmetric)
+                           n_out, words * (32 // bits), group_size, symmetric, bits)
 
 
 def assert_within_tolerance(y_gpu, y_ref, a_ref, what=""):

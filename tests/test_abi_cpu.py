@@ -21,7 +21,7 @@ P2 = 0x10002       # 2-byte but not 16-byte aligned
 
 def header_functions():
     text = open(HEADER, encoding="utf-8").read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(q4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(q[48]_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -124,3 +124,44 @@ def test_no_allocation_calls_in_the_boundary():
         text = open(os.path.join(csrc, f), encoding="utf-8").read()
         assert "hipMalloc" not in text and "hipFree" not in text, f
         assert "hipDeviceSynchronize" not in text and "hipStreamSynchronize" not in text, f
+
+
+def _qp_args(**kw):
+    a = dict(w=P16, n_out=8, n_in=256, g=128, sym=0, qw=P16, s=P2, z=P2)
+    a.update(kw)
+    return (a["w"], a["n_out"], a["n_in"], a["g"], a["sym"], a["qw"], a["s"], a["z"], None)
+
+
+@pytest.mark.parametrize("fn", ["q4_quantize_pack", "q8_quantize_pack"])
+def test_quantize_pack_rejects(L, fn):
+    f = getattr(L, fn)
+    assert f(*_qp_args(w=None)) == _lib.Q4_ERR_NULL
+    assert f(*_qp_args(g=48)) == _lib.Q4_ERR_GROUP
+    assert f(*_qp_args(n_in=100, g=100)) == _lib.Q4_ERR_GROUP          # per-channel needs n_in % 32 == 0
+    assert f(*_qp_args(n_in=0)) == _lib.Q4_ERR_SHAPE
+    assert f(*_qp_args(n_in=96, g=64)) == _lib.Q4_ERR_SHAPE            # 64 does not divide 96
+    assert f(*_qp_args(w=P2)) == _lib.Q4_ERR_ALIGN
+    # per-channel groups of any multiple-of-32 length are accepted: the
+    # first error is then the null pointer, not the group size
+    assert f(*_qp_args(n_in=96, g=96, qw=None)) == _lib.Q4_ERR_NULL
+    assert f(*_qp_args(n_in=11008, g=11008, w=P2)) == _lib.Q4_ERR_ALIGN
+
+
+@pytest.mark.parametrize("fn", ["q4_dequant", "q8_dequant"])
+def test_dequant_rejects(L, fn):
+    f = getattr(L, fn)
+    args = dict(qw=P16, s=P2, z=P2, n_out=8, n_in=256, g=128, out=P16)
+    def call(**kw):
+        a = dict(args); a.update(kw)
+        return f(a["qw"], a["s"], a["z"], a["n_out"], a["n_in"], a["g"], a["out"], None)
+    assert call(out=None) == _lib.Q4_ERR_NULL
+    assert call(g=512) == _lib.Q4_ERR_GROUP
+    assert call(out=P2) == _lib.Q4_ERR_ALIGN
+    assert call(n_in=160, g=160, qw=None) == _lib.Q4_ERR_NULL
+
+
+@pytest.mark.parametrize("fn", ["q4_gemv", "q4_gemm"])
+def test_linear_accepts_per_channel_groups(L, fn):
+    f = getattr(L, fn)
+    assert f(*_gemv_args(n_in=11008, g=11008, x=None)) == _lib.Q4_ERR_NULL
+    assert f(*_gemv_args(n_in=11008, g=11000)) == _lib.Q4_ERR_GROUP

@@ -1,0 +1,87 @@
+"""INT8 weights (W8A16) and per-channel groups on the GPU against the CPU oracle:
+quantize+pack and dequant bit for bit, the linear layers within the stated
+tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import w4a16_dequant_gemv_amd as w4
+from gpu_util import assert_bits_equal, assert_within_tolerance, f16_bits, qweight_from_oracle, to_dev, u32_bits
+from w4a16_dequant_gemv_amd import synthetic
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantize_both(orc, w, g, sym, bits):
+    qw = w4.quantize_pack(to_dev(w), g, sym, bits=bits)
+    torch.cuda.synchronize()
+    packed, scales, zeros, _ = orc.quantize_pack(w, g, sym, bits=bits)
+    return qw, packed, scales, zeros
+
+
+def _assert_same(qw, packed, scales, zeros, what):
+    assert_bits_equal(u32_bits(qw.qweight), packed, f"{what} packed")
+    assert_bits_equal(f16_bits(qw.scales), scales, f"{what} scales")
+    assert_bits_equal(f16_bits(qw.zeros), zeros, f"{what} zeros")
+
+
+@pytest.mark.parametrize("g", [32, 64, 128, 256, None])
+@pytest.mark.parametrize("sym", [False, True])
+def test_int8_quantize_normal_with_outliers(orc, g, sym):
+    w = synthetic.normal_weight(96, 2048, seed=201, std=0.02, n_outlier_cols=4)
+    gs = 2048 if g is None else g
+    qw, *ref = _quantize_both(orc, w, gs, sym, 8)
+    _assert_same(qw, *ref, f"int8 normal g={gs} sym={sym}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("shape", [(3, 32), (5, 96), (7, 11008), (16, 4096), (9, 2080), (1, 28672)])
+@pytest.mark.parametrize("sym", [False, True])
+def test_per_channel_quantize(orc, bits, shape, sym):
+    rng = np.random.default_rng(shape[1] + 7 * bits)
+    w = (rng.standard_t(3, size=shape) * 0.02).astype(np.float32)
+    w[0, :] = np.abs(w[0, :]) + 0.01                       # one all-positive row
+    qw, *ref = _quantize_both(orc, w, shape[1], sym, bits)
+    _assert_same(qw, *ref, f"per-channel {shape} bits={bits} sym={sym}")
+
+
+def test_int8_special_rows(orc):
+    """Exact ties at s = 1, one-signed rows, constant and tiny rows, per channel and per group."""
+    n = 32
+    rows = []
+    rows.append([-127.0, 128.0, 0.5, 1.5, 2.5, -0.5, -1.5, 3.5, -2.5, 100.5] + [0.0] * 22)
+    rows.append(list(np.linspace(0.5, 2.0, n)))
+    rows.append(list(np.linspace(-2.0, -0.5, n)))
+    for c in (0.75, -0.75, 0.0, -0.0, 3e-9, 2e-8):
+        rows.append([c] * n)
+    rows.append([1e-10 * i for i in range(n)])
+    rows.append([127.0, -126.5, 0.5, 1.5, 2.5, -0.5, -3.5, 5.5] + [0.0] * 24)
+    w = np.array(rows, dtype=np.float32)
+    for g in (32, n):
+        for sym in (False, True):
+            qw, *ref = _quantize_both(orc, w, g, sym, 8)
+            _assert_same(qw, *ref, f"int8 special g={g} sym={sym}")
+
+
+@pytest.mark.parametrize("bits,g", [(8, 128), (8, 32), (8, None), (4, None)])
+def test_dequant_bit_exact(orc, bits, g):
+    w = synthetic.student_t_weight(48, 4096, seed=203, group_size=128, const_frac=0.02, zero_frac=0.01)
+    gs = 4096 if g is None else g
+    packed, scales, zeros, _ = orc.quantize_pack(w, gs, False, bits=bits)
+    qw = qweight_from_oracle(packed, scales, zeros, gs, bits=bits)
+    wd = w4.dequant(qw)
+    torch.cuda.synchronize()
+    want = orc.dequant(packed, scales, zeros, gs, bits=bits)
+    assert np.array_equal(wd.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("n_out,n_in", [(100, 96), (300, 4096), (64, 11008), (129, 160)])
+@pytest.mark.parametrize("m,fn", [(1, "gemv"), (8, "gemv"), (16, "gemv"), (64, "gemm"), (300, "gemm")])
+def test_int4_per_channel_linear(orc, n_out, n_in, m, fn):
+    w = synthetic.normal_weight(n_out, n_in, seed=n_in + n_out, std=0.02, n_outlier_cols=2)
+    packed, scales, zeros, _ = orc.quantize_pack(w, n_in, False)
+    qw = qweight_from_oracle(packed, scales, zeros, n_in)
+    x = synthetic.activations_f16(m, n_in, seed=m + n_in)
+    y = getattr(w4, fn)(to_dev(x), qw)
+    y_ref, a_ref = orc.linear_from_packed(x.view(np.uint16), packed, scales, zeros, n_in)
+    assert_within_tolerance(y, y_ref, a_ref, f"{fn} per-channel m={m} {n_out}x{n_in}")

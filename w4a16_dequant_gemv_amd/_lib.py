@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libw4a16.so")
 
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_GROUP, Q4_ERR_ALIGN, Q4_ERR_HIP = range(6)
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # Every symbol the public header declares, with its ctypes signature.
 _p = ctypes.c_void_p
@@ -21,6 +21,8 @@ SIGNATURES = {
     "q4_dequant": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p]),
     "q4_gemv": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
     "q4_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
+    "q8_quantize_pack": (ctypes.c_int, [_p, _i64, _i64, _i32, _i32, _p, _p, _p, _p]),
+    "q8_dequant": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p]),
 }
 
 

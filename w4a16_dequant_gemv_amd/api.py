@@ -11,16 +11,19 @@ import torch
 from ._lib import W4A16Error, check, lib
 
 GROUP_SIZES = (32, 64, 128, 256)
+BITS = (4, 8)
 MAX_GEMV_ROWS = 16
 
 
 @dataclass
 class QuantizedWeight:
-    """Packed INT4 weight of a linear layer W[n_out, n_in].
+    """Packed INT4 (bits=4) or INT8 (bits=8) weight of a linear layer W[n_out, n_in].
 
-    qweight: int32 [n_out, n_in // 8]; element k of a row is the 4-bit code in
-             bits 4*(k % 8).. of word k // 8 (the int32 holds the u32 bits).
+    qweight: int32 [n_out, n_in * bits // 32]; element k of a row is the code
+             in bits bits*(k % (32/bits)).. of word k // (32/bits) (the int32
+             holds the u32 bits).
     scales, zeros: float16 [n_out, n_in // group_size]; w' = s * (code - z).
+    group_size == n_in is one scale per output channel.
     """
     qweight: torch.Tensor
     scales: torch.Tensor
@@ -29,6 +32,7 @@ class QuantizedWeight:
     n_in: int
     group_size: int
     symmetric: bool = False
+    bits: int = 4
 
     def nbytes(self):
         return (self.qweight.numel() * 4 + self.scales.numel() * 2 + self.zeros.numel() * 2)
@@ -57,58 +61,74 @@ def _same_device(*ts):
             raise W4A16Error("all tensors must be on the same GPU")
 
 
-def quantize_pack(w, group_size=128, symmetric=False, out=None):
-    """fp32 W [n_out, n_in] on the GPU -> QuantizedWeight (bit-exact INT4)."""
+def _prefix(bits):
+    if bits not in BITS:
+        raise W4A16Error(f"bits must be one of {BITS}, got {bits}")
+    return f"q{bits}_"
+
+
+def quantize_pack(w, group_size=128, symmetric=False, out=None, bits=4):
+    """fp32 W [n_out, n_in] on the GPU -> QuantizedWeight (bit-exact INT4 or INT8).
+    group_size None (or n_in) quantizes per output channel."""
     if w.dim() != 2:
         raise W4A16Error("w must be 2-D [n_out, n_in]")
     n_out, n_in = w.shape
-    if group_size not in GROUP_SIZES or n_in % group_size:
-        raise W4A16Error(f"group_size {group_size} must be one of {GROUP_SIZES} and divide n_in={n_in}")
+    if group_size is None:
+        group_size = n_in
+    per_channel = group_size == n_in and n_in % 32 == 0
+    if (group_size not in GROUP_SIZES and not per_channel) or n_in % group_size:
+        raise W4A16Error(f"group_size {group_size} must be one of {GROUP_SIZES} (dividing n_in={n_in}) "
+                         f"or n_in itself with n_in % 32 == 0")
+    prefix = _prefix(bits)
     _need(w, torch.float32, (n_out, n_in), "w")
     G = n_in // group_size
+    words = n_in * bits // 32
     if out is None:
         out = QuantizedWeight(
-            torch.empty((n_out, n_in // 8), dtype=torch.int32, device=w.device),
+            torch.empty((n_out, words), dtype=torch.int32, device=w.device),
             torch.empty((n_out, G), dtype=torch.float16, device=w.device),
             torch.empty((n_out, G), dtype=torch.float16, device=w.device),
-            n_out, n_in, group_size, bool(symmetric))
+            n_out, n_in, group_size, bool(symmetric), bits)
     else:
-        _need(out.qweight, torch.int32, (n_out, n_in // 8), "out.qweight")
+        _need(out.qweight, torch.int32, (n_out, words), "out.qweight")
         _need(out.scales, torch.float16, (n_out, G), "out.scales")
         _need(out.zeros, torch.float16, (n_out, G), "out.zeros")
-        out.group_size, out.symmetric = group_size, bool(symmetric)
+        out.group_size, out.symmetric, out.bits = group_size, bool(symmetric), bits
     _same_device(w, out.qweight, out.scales, out.zeros)
     with torch.cuda.device(w.device):
-        check(lib().q4_quantize_pack(w.data_ptr(), n_out, n_in, group_size, int(bool(symmetric)),
-                                     out.qweight.data_ptr(), out.scales.data_ptr(),
-                                     out.zeros.data_ptr(), _stream(w)), "q4_quantize_pack")
+        check(getattr(lib(), prefix + "quantize_pack")(
+            w.data_ptr(), n_out, n_in, group_size, int(bool(symmetric)), out.qweight.data_ptr(),
+            out.scales.data_ptr(), out.zeros.data_ptr(), _stream(w)), prefix + "quantize_pack")
     return out
 
 
 def _check_qw(qw):
-    _need(qw.qweight, torch.int32, (qw.n_out, qw.n_in // 8), "qweight")
+    _prefix(qw.bits)
+    _need(qw.qweight, torch.int32, (qw.n_out, qw.n_in * qw.bits // 32), "qweight")
     G = qw.n_in // qw.group_size
     _need(qw.scales, torch.float16, (qw.n_out, G), "scales")
     _need(qw.zeros, torch.float16, (qw.n_out, G), "zeros")
 
 
 def dequant(qw, out=None):
-    """QuantizedWeight -> fp32 W' [n_out, n_in], w' = s * (code - z), bit-exact."""
+    """QuantizedWeight (INT4 or INT8) -> fp32 W' [n_out, n_in], w' = s * (code - z), bit-exact."""
     _check_qw(qw)
     dev = qw.qweight.device
     if out is None:
         out = torch.empty((qw.n_out, qw.n_in), dtype=torch.float32, device=dev)
     _need(out, torch.float32, (qw.n_out, qw.n_in), "out")
     _same_device(qw.qweight, qw.scales, qw.zeros, out)
+    name = _prefix(qw.bits) + "dequant"
     with torch.cuda.device(dev):
-        check(lib().q4_dequant(qw.qweight.data_ptr(), qw.scales.data_ptr(), qw.zeros.data_ptr(),
-                               qw.n_out, qw.n_in, qw.group_size, out.data_ptr(), _stream(out)),
-              "q4_dequant")
+        check(getattr(lib(), name)(qw.qweight.data_ptr(), qw.scales.data_ptr(), qw.zeros.data_ptr(),
+                                   qw.n_out, qw.n_in, qw.group_size, out.data_ptr(), _stream(out)),
+              name)
     return out
 
 
-def _linear(fn_name, x, qw, out):
+def _linear(kind, x, qw, out):
     _check_qw(qw)
+    fn_name = _prefix(qw.bits) + kind
     if x.dim() != 2:
         raise W4A16Error("x must be 2-D [m, n_in]")
     m = x.shape[0]
@@ -128,12 +148,12 @@ def _linear(fn_name, x, qw, out):
 
 def gemv(x, qw, out=None):
     """Decode-shaped y = x W'^T, x fp16 [m <= 16, n_in] -> y fp16 [m, n_out]."""
-    return _linear("q4_gemv", x, qw, out)
+    return _linear("gemv", x, qw, out)
 
 
 def gemm(x, qw, out=None):
     """Prefill-shaped y = x W'^T for any m, tuned for large m."""
-    return _linear("q4_gemm", x, qw, out)
+    return _linear("gemm", x, qw, out)
 
 
 def linear(x, qw, out=None):

@@ -15,21 +15,24 @@ thread_local int g_last_hip_error = 0;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int check_group(int32_t group_size)
+// Groups of 32, 64, 128 or 256 elements, or one group per row (per-channel)
+// when the row is a whole number of 32-element slices.
+int check_group(int32_t group_size, int64_t n_in)
 {
     switch (group_size) {
     case 32: case 64: case 128: case 256: return Q4_OK;
-    default: return Q4_ERR_GROUP;
+    default: return (group_size == n_in && n_in % 32 == 0) ? Q4_OK : Q4_ERR_GROUP;
     }
 }
 
 // Shape rules common to every entry point: positive sizes within limits and
-// whole groups per row (the n_in % 8 packing rule follows from g >= 32).
+// whole groups per row (the n_in % 8 and % 4 packing rules follow from
+// n_in % 32 == 0).
 int check_weight_shape(int64_t n_out, int64_t n_in, int32_t group_size)
 {
     if (n_out <= 0 || n_in <= 0 || n_out > kMaxOut || n_in > kMaxIn) return Q4_ERR_SHAPE;
     if (n_out * n_in > kMaxElems) return Q4_ERR_SHAPE;
-    if (int rc = check_group(group_size)) return rc;
+    if (int rc = check_group(group_size, n_in)) return rc;
     if (n_in % group_size != 0) return Q4_ERR_SHAPE;
     return Q4_OK;
 }
@@ -67,7 +70,8 @@ const char *q4_strerror(int status)
     case Q4_ERR_NULL: return "a required pointer is NULL";
     case Q4_ERR_SHAPE: return "invalid shape: a size is <= 0 or too large, n_in is not a multiple "
                               "of group_size, or m is outside the entry point's range";
-    case Q4_ERR_GROUP: return "unsupported group_size (supported: 32, 64, 128, 256)";
+    case Q4_ERR_GROUP: return "unsupported group_size (supported: 32, 64, 128, 256, and n_in "
+                              "itself for one group per output channel when n_in % 32 == 0)";
     case Q4_ERR_ALIGN: return "misaligned pointer: w, w_out, qweight and x need 16 bytes, fp16 "
                               "arrays 2 bytes";
     case Q4_ERR_HIP: return "the HIP runtime refused the launch (see q4_last_hip_error)";
@@ -77,27 +81,61 @@ const char *q4_strerror(int status)
 
 int q4_last_hip_error(void) { return g_last_hip_error; }
 
-int q4_quantize_pack(const float *w, int64_t n_out, int64_t n_in, int32_t group_size,
-                     int32_t symmetric, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
-                     void *stream)
+}  // extern "C"
+
+namespace {
+
+int quantize_pack(int bits, const float *w, int64_t n_out, int64_t n_in, int32_t group_size,
+                  int32_t symmetric, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                  void *stream)
 {
     if (!w || !qweight || !scales || !zeros) return Q4_ERR_NULL;
     if (int rc = check_weight_shape(n_out, n_in, group_size)) return rc;
     if (!aligned(w, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
         return Q4_ERR_ALIGN;
-    return finish(q4_launch_quantize_pack(w, n_out, n_in, group_size, symmetric != 0, qweight,
+    return finish(q4_launch_quantize_pack(w, n_out, n_in, group_size, bits, symmetric != 0, qweight,
                                           scales, zeros, (hipStream_t)stream));
 }
 
-int q4_dequant(const uint32_t *qweight, const uint16_t *scales, const uint16_t *zeros,
-               int64_t n_out, int64_t n_in, int32_t group_size, float *w_out, void *stream)
+int dequant(int bits, const uint32_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+            int64_t n_out, int64_t n_in, int32_t group_size, float *w_out, void *stream)
 {
     if (!qweight || !scales || !zeros || !w_out) return Q4_ERR_NULL;
     if (int rc = check_weight_shape(n_out, n_in, group_size)) return rc;
     if (!aligned(qweight, 16) || !aligned(w_out, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
         return Q4_ERR_ALIGN;
-    return finish(q4_launch_dequant(qweight, scales, zeros, n_out, n_in, group_size, w_out,
+    return finish(q4_launch_dequant(qweight, scales, zeros, n_out, n_in, group_size, bits, w_out,
                                     (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_quantize_pack(const float *w, int64_t n_out, int64_t n_in, int32_t group_size,
+                     int32_t symmetric, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                     void *stream)
+{
+    return quantize_pack(4, w, n_out, n_in, group_size, symmetric, qweight, scales, zeros, stream);
+}
+
+int q8_quantize_pack(const float *w, int64_t n_out, int64_t n_in, int32_t group_size,
+                     int32_t symmetric, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                     void *stream)
+{
+    return quantize_pack(8, w, n_out, n_in, group_size, symmetric, qweight, scales, zeros, stream);
+}
+
+int q4_dequant(const uint32_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+               int64_t n_out, int64_t n_in, int32_t group_size, float *w_out, void *stream)
+{
+    return dequant(4, qweight, scales, zeros, n_out, n_in, group_size, w_out, stream);
+}
+
+int q8_dequant(const uint32_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+               int64_t n_out, int64_t n_in, int32_t group_size, float *w_out, void *stream)
+{
+    return dequant(8, qweight, scales, zeros, n_out, n_in, group_size, w_out, stream);
 }
 
 int q4_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_m = wave / WN, wave_n = wave % WN;
     const int words_per_row = n_in >> 3;
-    const int groups_per_row = n_in >> group_shift;
+    const int groups_per_row = group_shift >= 31 ? 1 : n_in >> group_shift;   // 31: one group per row
     const int ksteps = n_in / BK;                       // full 64-wide steps
 
     // Per-tile buffer resources covering the tile's rows; lanes add constant
@@ -455,8 +455,11 @@ hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
                           int group_size, uint16_t *y, hipStream_t stream)
 {
+    // group k of a row is k >> shift; a per-channel group of any other
+    // length than a power of two uses shift 31 (every k in group 0)
     int shift = 0;
     while ((1 << shift) < group_size) ++shift;
+    if ((1 << shift) != group_size) shift = 31;
     return launch_gemm<256, 128, 4, 1>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
                                           shift, y, stream);
 }

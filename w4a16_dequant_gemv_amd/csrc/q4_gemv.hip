@@ -25,7 +25,7 @@
 // leaves every dot product unchanged.
 //
 // Two ways of forming B:
-//  * group_size >= 128 (every 128-wide k block lies in one group):
+//  * group_size 128 or 256 (every 128-wide k block lies in one group):
 //    masking a packed word with 0x000F000F leaves codes (c_t, c_{t+4}) as the
 //    fp16 bit patterns of the subnormals c * 2^-24 -- exact values, two
 //    codes per AND.  Masking with 0x00F000F0 gives c * 2^-20.  So B costs
@@ -37,7 +37,9 @@
 //    MFMA chain against B = 2^-24.  Nothing is rounded before the fp32
 //    accumulation; the subtraction is between terms of similar size (codes
 //    and z are both in 0..15), so it loses no accuracy to speak of.
-//  * group_size 32 or 64 (a block spans several groups): the classic form,
+//  * group_size 32 or 64 (a block spans several groups), or one group per
+//    row (per-channel, where most codes equal z and the fold would cancel
+//    large terms): the classic form,
 //    OR-ing codes into the half 1024 (0x6400), subtracting 1024 + z (exact)
 //    and multiplying by s in fp16 (the only rounding, 2^-11 relative).
 //
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
 
     const int m = geo.m, n_out = geo.n_out, n_in = geo.n_in, gshift = geo.group_shift;
     const int kblocks = geo.kblocks;
-    const int groups_win = (WB * 128) >> gshift;
+    const int groups_win = max(1, (WB * 128) >> gshift);
     const int x_buf_bytes = m * geo.x_row_bytes;
     const int sz_buf_bytes = ROWS * geo.sz_stride * 4;
     char *x_lds = lds;                                   // [2][m][x_row_bytes]
@@ -546,7 +548,7 @@ Geometry make_geometry(int m, int n_out, int n_in, int group_shift)
     g.n_in = n_in;
     g.group_shift = group_shift;
     g.words_per_row = n_in >> 3;
-    g.groups_per_row = n_in >> group_shift;
+    g.groups_per_row = group_shift >= 31 ? 1 : n_in >> group_shift;   // 31: one group per row
     g.kblocks = (n_in + 127) >> 7;
     g.last_full_quarter = ((n_in - ((g.kblocks - 1) << 7)) >> 5) - 1;
     g.sz_stride = 0;
@@ -676,9 +678,17 @@ hipError_t q4_launch_gemv(const uint16_t *x, const uint32_t *qweight, const uint
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
                           int group_size, uint16_t *y, hipStream_t stream)
 {
+    // group k of a row is k >> shift; a per-channel group of any other
+    // length than a power of two uses shift 31 (every k in group 0)
     int shift = 0;
     while ((1 << shift) < group_size) ++shift;
-    return group_size >= 128
+    if ((1 << shift) != group_size) shift = 31;
+    // The fold applies s and z once per 128-wide block after summing raw
+    // codes, subtracting z * sum(x) from the code sum; with one scale per
+    // row (per-channel) most codes sit at z and that subtraction would
+    // cancel terms far larger than the result, so per-channel weights take
+    // the exact-subtraction form.
+    return (group_size == 128 || group_size == 256)
                ? dispatch<true>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream)
                : dispatch<false>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
 }
