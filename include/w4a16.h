@@ -162,6 +162,25 @@ int q8_dequant(const uint32_t *qweight, const uint16_t *scales, const uint16_t *
                int64_t n_out, int64_t n_in, int32_t group_size, float *w_out,
                void *stream);
 
+/*
+ * Decode-shaped W8A16 linear layer: y = x W'^T for 1 <= m <= 16 with INT8
+ * weights packed as q8_quantize_pack writes them; the codes are dequantized
+ * in registers as (1024 + c) - (1024 + z), exact in fp16, times s.  Same
+ * error bound, alignment rules and m range as q4_gemv.
+ */
+int q8_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
+            int32_t group_size, uint16_t *y, void *stream);
+
+/*
+ * Prefill-shaped W8A16 linear layer for any m >= 1: INT8 weight tiles are
+ * dequantized into LDS as fp16 and fed to the fp16 matrix cores, as in
+ * q4_gemm.  Same error bound and alignment rules as q4_gemv.
+ */
+int q8_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
+            int32_t group_size, uint16_t *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

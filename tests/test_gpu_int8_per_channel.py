@@ -85,3 +85,49 @@ def test_int4_per_channel_linear(orc, n_out, n_in, m, fn):
     y = getattr(w4, fn)(to_dev(x), qw)
     y_ref, a_ref = orc.linear_from_packed(x.view(np.uint16), packed, scales, zeros, n_in)
     assert_within_tolerance(y, y_ref, a_ref, f"{fn} per-channel m={m} {n_out}x{n_in}")
+
+
+Q8_SHAPES = [(100, 96, 32), (128, 256, 128), (300, 4096, None), (64, 11008, None),
+             (129, 1088, 64), (256, 2048, 256), (200, 1120, 32), (97, 160, None)]
+
+
+@pytest.mark.parametrize("n_out,n_in,g", Q8_SHAPES)
+@pytest.mark.parametrize("m,fn", [(1, "gemv"), (3, "gemv"), (8, "gemv"), (16, "gemv"),
+                                  (64, "gemm"), (300, "gemm")])
+@pytest.mark.parametrize("sym", [False, True])
+def test_int8_linear(orc, n_out, n_in, g, m, fn, sym):
+    gs = n_in if g is None else g
+    w = synthetic.student_t_weight(n_out, n_in, seed=5 * n_in + n_out, group_size=32)
+    packed, scales, zeros, _ = orc.quantize_pack(w, gs, sym, bits=8)
+    qw = qweight_from_oracle(packed, scales, zeros, gs, sym, bits=8)
+    x = synthetic.activations_f16(m, n_in, seed=m + 3 * n_in)
+    y = getattr(w4, fn)(to_dev(x), qw)
+    y_ref, a_ref = orc.linear_from_packed(x.view(np.uint16), packed, scales, zeros, gs, bits=8)
+    assert_within_tolerance(y, y_ref, a_ref, f"q8 {fn} m={m} {n_out}x{n_in} g={gs} sym={sym}")
+
+
+@pytest.mark.parametrize("fn,m", [("gemv", 3), ("gemm", 40)])
+@pytest.mark.parametrize("g", [32, None])
+def test_int8_one_hot_is_bitwise(orc, fn, m, g):
+    """x = e_k selects column k of W': y = fp16(w'[:, k]) exactly, for INT8 codes."""
+    n_out, n_in = 160, 1056
+    gs = n_in if g is None else g
+    w = synthetic.normal_weight(n_out, n_in, seed=207, n_outlier_cols=2)
+    packed, scales, zeros, _ = orc.quantize_pack(w, gs, False, bits=8)
+    wd = orc.dequant(packed, scales, zeros, gs, bits=8)
+    qw = qweight_from_oracle(packed, scales, zeros, gs, bits=8)
+    ks = (0, 1, 3, 4, 15, 16, 31, 32, 63, 64, 1023, 1024, 1055)
+    x = np.zeros((m, n_in), dtype=np.float16)
+    for r, k in enumerate(ks[:m] if m < len(ks) else ks):
+        x[r, k] = 1.0
+    y = f16_bits(getattr(w4, fn)(to_dev(x), qw))
+    for r, k in enumerate(ks[:m] if m < len(ks) else ks):
+        assert_bits_equal(y[r], wd[:, k].astype(np.float16).view(np.uint16), f"q8 {fn} one-hot k={k}")
+    for r in range(min(m, len(ks)), m):
+        assert np.all(y[r] == 0)
+
+
+def test_int8_rejects_bad_group(orc):
+    w = torch.zeros((8, 96), dtype=torch.float32, device="cuda")
+    with pytest.raises(w4.W4A16Error):
+        w4.quantize_pack(w, 48, bits=8)

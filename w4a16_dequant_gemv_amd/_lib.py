@@ -23,6 +23,8 @@ SIGNATURES = {
     "q4_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
     "q8_quantize_pack": (ctypes.c_int, [_p, _i64, _i64, _i32, _i32, _p, _p, _p, _p]),
     "q8_dequant": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p]),
+    "q8_gemv": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
+    "q8_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
 }
 
 

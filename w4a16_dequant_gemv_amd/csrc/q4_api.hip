@@ -144,7 +144,17 @@ int q4_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
 {
     if (int rc = check_linear(x, qweight, scales, zeros, m, n_out, n_in, group_size, y, 16))
         return rc;
-    return finish(q4_launch_gemv(x, qweight, scales, zeros, m, n_out, n_in, group_size, y,
+    return finish(q4_launch_gemv(x, qweight, scales, zeros, m, n_out, n_in, group_size, 4, y,
+                                 (hipStream_t)stream));
+}
+
+int q8_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in, int32_t group_size,
+            uint16_t *y, void *stream)
+{
+    if (int rc = check_linear(x, qweight, scales, zeros, m, n_out, n_in, group_size, y, 16))
+        return rc;
+    return finish(q4_launch_gemv(x, qweight, scales, zeros, m, n_out, n_in, group_size, 8, y,
                                  (hipStream_t)stream));
 }
 
@@ -154,7 +164,17 @@ int q4_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
 {
     if (int rc = check_linear(x, qweight, scales, zeros, m, n_out, n_in, group_size, y, kMaxRows))
         return rc;
-    return finish(q4_launch_gemm(x, qweight, scales, zeros, m, n_out, n_in, group_size, y,
+    return finish(q4_launch_gemm(x, qweight, scales, zeros, m, n_out, n_in, group_size, 4, y,
+                                 (hipStream_t)stream));
+}
+
+int q8_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+            const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in, int32_t group_size,
+            uint16_t *y, void *stream)
+{
+    if (int rc = check_linear(x, qweight, scales, zeros, m, n_out, n_in, group_size, y, kMaxRows))
+        return rc;
+    return finish(q4_launch_gemm(x, qweight, scales, zeros, m, n_out, n_in, group_size, 8, y,
                                  (hipStream_t)stream));
 }
 

@@ -80,6 +80,20 @@ __device__ __forceinline__ u32x4 dequant_word_natural(uint32_t w, f16x2 bias, f1
     return r;
 }
 
+// Four codes of one INT8 word -> four fp16 weights s * (c - z) in natural
+// order, as two dwords (c0, c1), (c2, c3): each byte is placed next to a zero
+// byte and OR-ed into the half 1024; (1024 + c) - (1024 + z) is exact for
+// codes up to 255 and the product with s is the only rounding.
+__device__ __forceinline__ u32x2 dequant_byte_word(uint32_t w, f16x2 bias, f16x2 scale)
+{
+    u32x2 r;
+    r[0] = __builtin_amdgcn_perm(0u, w, 0x0C010C00u) | 0x64006400u;
+    r[1] = __builtin_amdgcn_perm(0u, w, 0x0C030C02u) | 0x64006400u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r[j] = bitcast<uint32_t>((bitcast<f16x2>(r[j]) - bias) * scale);
+    return r;
+}
+
 // Chunk permutation of LDS row r, a function of r & 15.  Its low two bits
 // differ across any 4 consecutive rows and across the 4 even (or 4 odd) rows
 // of an aligned group of 8; the whole value differs across any aligned group
@@ -105,7 +119,7 @@ __device__ __forceinline__ void interleave()
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BITS = 4>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -116,13 +130,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     constexpr int NW = WM * WN, THREADS = 64 * NW;
     constexpr int WT_M = BM / WM, WT_N = BN / WN;
     constexpr int TM = WT_M / 32, TN = WT_N / 32;
+    // A 16-byte slice of packed codes holds 128/BITS codes (32 INT4, 16 INT8),
+    // i.e. CHS fp16 LDS chunks; a row's 64 codes per step are SPR slices.
+    constexpr int SPR = BITS / 2, CPS = 128 / BITS, CHS = CPS / 8;
     constexpr int A_CHUNKS = BM * 8 / THREADS;         // 16-byte x chunks per lane per step
-    constexpr int B_SLICES = BN * 2 / THREADS;         // 16-byte code slices per lane per step
+    constexpr int B_SLICES = BN * SPR / THREADS;       // 16-byte code slices per lane per step
     constexpr int A_PART = A_CHUNKS / KSUB;            // x chunks stored per substep
     constexpr int B_PART = B_SLICES;                   // packed words dequantized per substep
     static_assert(A_CHUNKS * THREADS == BM * 8 && A_PART * KSUB == A_CHUNKS,
                   "x tile does not split evenly");
-    static_assert(B_SLICES * THREADS == BN * 2, "weight tile does not split evenly");
+    static_assert(B_SLICES * THREADS == BN * SPR, "weight tile does not split evenly");
+    static_assert(BITS == 4 || (BITS == 8 && B_PART % 2 == 0), "INT8 stores pair words into chunks");
     static_assert(TM * 32 == WT_M && TN * 32 == WT_N, "wave tile not a multiple of 32");
     static_assert(THREADS % 128 == 0, "row swizzles assume 16-row lane strides");
     constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
@@ -148,7 +166,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_m = wave / WN, wave_n = wave % WN;
-    const int words_per_row = n_in >> 3;
+    const int words_per_row = n_in * BITS / 32;
     const int groups_per_row = group_shift >= 31 ? 1 : n_in >> group_shift;   // 31: one group per row
     const int ksteps = n_in / BK;                       // full 64-wide steps
 
@@ -178,19 +196,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     }
 #pragma unroll
     for (int i = 0; i < B_SLICES; ++i) {
-        const int c = tid + i * THREADS;                   // row c/2, half c%2
-        const int r = min(c >> 1, n_out - 1 - n0);
-        woff[i] = (uint32_t)r * (uint32_t)words_per_row * 4u + (uint32_t)(c & 1) * 16u;
-        soff[i] = ((uint32_t)r * (uint32_t)groups_per_row + (uint32_t)(((c & 1) * 32) >> group_shift)) * 2u;
+        const int c = tid + i * THREADS;                   // row c/SPR, slice c%SPR of the step
+        const int r = min(c / SPR, n_out - 1 - n0);
+        woff[i] = (uint32_t)r * (uint32_t)words_per_row * 4u + (uint32_t)(c % SPR) * 16u;
+        soff[i] = ((uint32_t)r * (uint32_t)groups_per_row + (uint32_t)(((c % SPR) * CPS) >> group_shift)) * 2u;
     }
     // LDS byte offsets within a stage: x chunk i of this lane, weight chunk
     // j of slice i, fragment rows.  Rows of chunk i differ by multiples of 16
     // from those of chunk 0, so they share its swizzle.
-    const int a_row = tid >> 3, b_row = tid >> 1, b_half = tid & 1;
+    static_assert((THREADS / SPR) % 16 == 0, "weight rows of slice i must keep slice 0's swizzle");
+    const int a_row = tid >> 3, b_row = tid / SPR, b_part = tid % SPR;
     const uint32_t a_st = a_row * 128 + (((tid & 7) ^ swz(a_row)) * 16);
-    uint32_t b_st[4];
+    uint32_t b_st[CHS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b_st[j] = A_BYTES + b_row * 128 + (((b_half * 4 + j) ^ swz(b_row)) * 16);
+    for (int j = 0; j < CHS; ++j) b_st[j] = A_BYTES + b_row * 128 + (((b_part * CHS + j) ^ swz(b_row)) * 16);
+    constexpr int B_ROW_STEP = THREADS / SPR * 128;     // LDS bytes between the rows of slices i and i+1
     const int frow = lane & 31, fkg = lane >> 5, fswz = swz(frow);
     const uint32_t fa = (wave_m * WT_M + frow) * 128, fb = A_BYTES + (wave_n * WT_N + frow) * 128;
 
@@ -216,7 +236,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         const int gk = ((kt * BK) >> group_shift) * 2;
 #pragma unroll
         for (int i = 0; i < B_SLICES; ++i) {
-            g.w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK / 2), 0);
+            g.w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK * BITS / 8), 0);
             g.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff[i], gk, 0);
             g.z[i] = __builtin_amdgcn_raw_buffer_load_b16(zr, soff[i], gk, 0);
         }
@@ -233,14 +253,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
             const int i = p * A_PART + q;
             *reinterpret_cast<u32x4 *>(smem + buf + a_st + i * THREADS * 16) = g.a[i];
         }
+        if (BITS == 4) {
 #pragma unroll
-        for (int q = 0; q < B_PART; ++q) {
-            const int wd = p * B_PART + q, i = wd >> 2, j = wd & 3;
-            const _Float16 sv = bitcast<_Float16>((uint16_t)g.s[i]);
-            const _Float16 zb = bitcast<_Float16>((uint16_t)g.z[i]) + (_Float16)1024.0f;
-            const f16x2 scale = {sv, sv}, bias = {zb, zb};
-            *reinterpret_cast<u32x4 *>(smem + buf + b_st[j] + i * THREADS * 64) =
-                dequant_word_natural(g.w[i][j], bias, scale);
+            for (int q = 0; q < B_PART; ++q) {
+                const int wd = p * B_PART + q, i = wd >> 2, j = wd & 3;
+                const _Float16 sv = bitcast<_Float16>((uint16_t)g.s[i]);
+                const _Float16 zb = bitcast<_Float16>((uint16_t)g.z[i]) + (_Float16)1024.0f;
+                const f16x2 scale = {sv, sv}, bias = {zb, zb};
+                *reinterpret_cast<u32x4 *>(smem + buf + b_st[j] + i * B_ROW_STEP) =
+                    dequant_word_natural(g.w[i][j], bias, scale);
+            }
+        } else {
+            // two INT8 words (eight codes) make one fp16 chunk
+#pragma unroll
+            for (int q = 0; q < B_PART; q += 2) {
+                const int wd = p * B_PART + q, i = wd >> 2, j = wd & 3;
+                const _Float16 sv = bitcast<_Float16>((uint16_t)g.s[i]);
+                const _Float16 zb = bitcast<_Float16>((uint16_t)g.z[i]) + (_Float16)1024.0f;
+                const f16x2 scale = {sv, sv}, bias = {zb, zb};
+                const u32x2 lo = dequant_byte_word(g.w[i][j], bias, scale);
+                const u32x2 hi = dequant_byte_word(g.w[i][j + 1], bias, scale);
+                *reinterpret_cast<u32x4 *>(smem + buf + b_st[j >> 1] + i * B_ROW_STEP) =
+                    u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
         }
     };
     auto store_all = [&](const Regs &g, uint32_t buf) {
@@ -352,19 +387,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
             if ((tid & 7) < 4)
                 *reinterpret_cast<u32x4 *>(smem + a_st + i * THREADS * 16) =
                     __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * (BK * 2), 0);
-        if (b_half == 0) {
+        if (b_part < SPR / 2) {                 // the slices of k = 0 .. 31 of the step
             const int gk = ((kt * BK) >> group_shift) * 2;
 #pragma unroll
             for (int i = 0; i < B_SLICES; ++i) {
-                const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK / 2), 0);
+                const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK * BITS / 8), 0);
                 const _Float16 sv = bitcast<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(sr, soff[i], gk, 0));
                 const _Float16 zb = bitcast<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(zr, soff[i], gk, 0)) +
                                     (_Float16)1024.0f;
                 const f16x2 scale = {sv, sv}, bias = {zb, zb};
+                if (BITS == 4) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<u32x4 *>(smem + b_st[j] + i * THREADS * 64) =
-                        dequant_word_natural(w[j], bias, scale);
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<u32x4 *>(smem + b_st[j] + i * B_ROW_STEP) =
+                            dequant_word_natural(w[j], bias, scale);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; j += 2) {
+                        const u32x2 lo = dequant_byte_word(w[j], bias, scale);
+                        const u32x2 hi = dequant_byte_word(w[j + 1], bias, scale);
+                        *reinterpret_cast<u32x4 *>(smem + b_st[j >> 1] + i * B_ROW_STEP) =
+                            u32x4{lo[0], lo[1], hi[0], hi[1]};
+                    }
+                }
             }
         }
         __syncthreads();
@@ -433,14 +478,14 @@ hipError_t allow_lds(K kernel, size_t bytes)
     return e;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BITS = 4>
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                        const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
                        uint16_t *y, hipStream_t stream)
 {
     const int tiles_m = (m + BM - 1) / BM, tiles_n = (n_out + BN - 1) / BN;
     const size_t lds = kStages * (size_t)(BM + BN) * 128;
-    auto kernel = gemm_kernel<BM, BN, WM, WN>;
+    auto kernel = gemm_kernel<BM, BN, WM, WN, BITS>;
     const hipError_t e = allow_lds(kernel, lds);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
@@ -453,13 +498,16 @@ hipError_t launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_
 
 hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, uint16_t *y, hipStream_t stream)
+                          int group_size, int bits, uint16_t *y, hipStream_t stream)
 {
     // group k of a row is k >> shift; a per-channel group of any other
     // length than a power of two uses shift 31 (every k in group 0)
     int shift = 0;
     while ((1 << shift) < group_size) ++shift;
     if ((1 << shift) != group_size) shift = 31;
-    return launch_gemm<256, 128, 4, 1>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
-                                          shift, y, stream);
+    if (bits == 8)
+        return launch_gemm<256, 128, 4, 1, 8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
+                                              shift, y, stream);
+    return launch_gemm<256, 128, 4, 1>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift,
+                                       y, stream);
 }

@@ -43,6 +43,14 @@
 //    OR-ing codes into the half 1024 (0x6400), subtracting 1024 + z (exact)
 //    and multiplying by s in fp16 (the only rounding, 2^-11 relative).
 //
+// INT8 weights (BITS = 8, W8A16).  A lane's 32 codes of a block are 32
+// bytes, two 16-byte loads (eight words).  MFMA t takes words 2t and 2t+1:
+// masking with 0x00FF00FF before and after a shift by 8 leaves the byte
+// pairs (k, k+2) and (k+1, k+3), OR-ed into the half 1024, so x is staged
+// with the middle two of every four values swapped; z is subtracted exactly
+// and s multiplied in fp16, as in the second form above (8-bit weights never
+// take the fold).
+//
 // Work split.  A workgroup of SPLIT waves owns CT tiles of 16 output
 // channels.  Its k blocks are dealt out in stages of SPLIT * UNROLL: in stage
 // i wave w takes blocks (i * SPLIT + w) * UNROLL + u, so at any moment the
@@ -72,10 +80,11 @@ struct Geometry {
     int sz_vector;          // scale/zero arrays allow 16-byte loads
 };
 
-// Per-lane weight registers of one stage: UNROLL blocks x CT tiles.
-template <int CT, int UNROLL>
+// Per-lane weight registers of one stage: UNROLL blocks x CT tiles x the
+// 16-byte loads of one block (BITS / 4: one for INT4, two for INT8).
+template <int CT, int UNROLL, int BITS = 4>
 struct Stage {
-    u32x4 w[UNROLL][CT];
+    u32x4 w[UNROLL][CT * (BITS / 4)];
 };
 
 // Eight consecutive x values (four dwords) -> the dword (x[t], x[t+4]) used
@@ -91,24 +100,53 @@ __device__ __forceinline__ uint32_t pick_pair(const u32x4 &v, int t)
 // Four consecutive 16-byte x chunks (32 values at k = 32q ..) -> their four
 // fragment dwords-quads, written at t*64 + q*16 (conflict-free: consecutive
 // chunks land in consecutive 16-byte slots).
+template <int BITS = 4>
 __device__ __forceinline__ void store_x_chunk(char *row_block, int quarter, const u32x4 c[4])
 {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         u32x4 d;
+        if (BITS == 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) d[j] = pick_pair(c[j], t);
+            for (int j = 0; j < 4; ++j) d[j] = pick_pair(c[j], t);
+        } else {
+            // INT8: MFMA t takes x[8t .. 8t+7] as (0,2) (1,3) (4,6) (5,7)
+            d[0] = __builtin_amdgcn_perm(c[t][1], c[t][0], 0x05040100u);
+            d[1] = __builtin_amdgcn_perm(c[t][1], c[t][0], 0x07060302u);
+            d[2] = __builtin_amdgcn_perm(c[t][3], c[t][2], 0x05040100u);
+            d[3] = __builtin_amdgcn_perm(c[t][3], c[t][2], 0x07060302u);
+        }
         *reinterpret_cast<u32x4 *>(row_block + t * 64 + quarter * 16) = d;
     }
 }
 
 // One 128-wide k block of CT tiles: B from the packed words, A from LDS,
 // scale|zero from LDS; `valid` false contributes nothing.
-template <int CT, bool FOLD>
-__device__ __forceinline__ void process_block(f32x4 acc[CT], const f16x8 a[4], const u32x4 w[CT],
+template <int CT, bool FOLD, int BITS = 4>
+__device__ __forceinline__ void process_block(f32x4 acc[CT], const f16x8 a[4], const u32x4 *w,
                                               const uint32_t sz[CT], bool valid)
 {
-    if (FOLD) {
+    if (BITS == 8) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const _Float16 s = valid ? bitcast<_Float16>((uint16_t)sz[c]) : (_Float16)0.0f;
+            const _Float16 zb = bitcast<_Float16>((uint16_t)(sz[c] >> 16)) + (_Float16)1024.0f;
+            const f16x2 scale = {s, s}, bias = {zb, zb};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 &l = w[c * 2 + (t >> 1)];
+                const uint32_t w0 = l[(2 * t) & 3], w1 = l[(2 * t + 1) & 3];
+                u32x4 b;
+                b[0] = (w0 & 0x00FF00FFu) | 0x64006400u;           // k = 8t + 0, 8t + 2
+                b[1] = ((w0 >> 8) & 0x00FF00FFu) | 0x64006400u;    // 8t + 1, 8t + 3
+                b[2] = (w1 & 0x00FF00FFu) | 0x64006400u;           // 8t + 4, 8t + 6
+                b[3] = ((w1 >> 8) & 0x00FF00FFu) | 0x64006400u;    // 8t + 5, 8t + 7
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = bitcast<uint32_t>((bitcast<f16x2>(b[j]) - bias) * scale);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bitcast<f16x8>(b), acc[c], 0, 0, 0);
+            }
+        }
+    } else if (FOLD) {
         // X = 2^-24 * sum of this lane-row's x over the block.
         const f16x8 tiny = bitcast<f16x8>(u32x4{0x00010001u, 0x00010001u, 0x00010001u, 0x00010001u});
         f32x4 xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], tiny, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -200,8 +238,9 @@ __device__ __forceinline__ void finish(f32x4 acc[CT], char *lds, uint16_t *y, in
 // Per-lane weight addressing shared by both kernels: a wave-uniform base
 // plus fixed 32-bit lane offsets.  Rows past n_out are clamped to a valid
 // row (their outputs are never stored).
-template <int CT>
+template <int CT, int BITS = 4>
 struct WeightAddr {
+    static constexpr int WPQ = BITS;          // packed words per lane per block (one quarter's 32 codes)
     const char *qbase;
     const char *xsafe;      // 16-byte-aligned, L2-hot target for loads past the end
     uint32_t woff[CT];
@@ -218,7 +257,7 @@ struct WeightAddr {
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
             const int r = min(t * 16 + col, geo.n_out - 1 - row0);
-            woff[t] = (uint32_t)(r * geo.words_per_row + q * 4) * 4u;
+            woff[t] = (uint32_t)(r * geo.words_per_row + q * WPQ) * 4u;
         }
     }
     // A block past the end, or a padding quarter of a partial last block.
@@ -226,14 +265,15 @@ struct WeightAddr {
     {
         return kb < kblocks && !(kb == kblocks - 1 && quarter > last_full_quarter);
     }
-    __device__ __forceinline__ u32x4 load(int kb, int t) const
+    // Load l (0 .. BITS/4 - 1) of block kb of tile t.
+    __device__ __forceinline__ u32x4 load(int kb, int t, int l = 0) const
     {
         // a padding quarter is moved back onto the last whole slice; the
         // offsets are summed as 32-bit values before meeting the base, so the
         // wrapped negative part cancels
         const int qs = (kb == kblocks - 1 && quarter > last_full_quarter) ? last_full_quarter - quarter : 0;
         const bool inside = kb < kblocks;
-        const uint32_t off = inside ? woff[t] + (uint32_t)(kb * 16 + qs * 4) * 4u : 0u;
+        const uint32_t off = inside ? woff[t] + (uint32_t)(kb * 4 * WPQ + qs * WPQ + l * 4) * 4u : 0u;
         const char *base = inside ? qbase : xsafe;
         return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + off));
     }
@@ -242,7 +282,7 @@ struct WeightAddr {
 // ---------------------------------------------------------------------------
 // Resident kernel: x and all scale|zero pairs staged once in LDS.
 // ---------------------------------------------------------------------------
-template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD>
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4>
 __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -267,13 +307,17 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     const int quarter = lane >> 4;
     const int row0 = blockIdx.x * ROWS;
 
-    WeightAddr<CT> wa;
+    constexpr int LPB = BITS / 4;                  // 16-byte weight loads per block per tile
+    WeightAddr<CT, BITS> wa;
     wa.init(qweight, x, geo, row0, col, quarter);
-    auto load_stage = [&](Stage<CT, UNROLL> &st, int i) {
+    auto load_stage = [&](Stage<CT, UNROLL, BITS> &st, int i) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-            for (int t = 0; t < CT; ++t) st.w[u][t] = wa.load((i * SPLIT + wave) * UNROLL + u, t);
+            for (int t = 0; t < CT; ++t)
+#pragma unroll
+                for (int l = 0; l < LPB; ++l)
+                    st.w[u][t * LPB + l] = wa.load((i * SPLIT + wave) * UNROLL + u, t, l);
     };
 
     // ---- staging of x (chunk c = (row, block, quarter) holds 32 values) and
@@ -300,7 +344,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     auto x_store = [&](int c, const u32x4 v[4]) {
         if (c < n_chunks) {
             const int r = c / (kblocks * 4), rem = c % (kblocks * 4);
-            store_x_chunk(x_lds + r * geo.x_row_bytes + (rem >> 2) * 256, rem & 3, v);
+            store_x_chunk<BITS>(x_lds + r * geo.x_row_bytes + (rem >> 2) * 256, rem & 3, v);
         }
     };
     // vector path: the rows are one contiguous, 16-byte-aligned run of both
@@ -339,7 +383,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     u32x4 xv[4], s8, z8;
     x_load(tid, xv);
     sz_load(tid, s8, z8);
-    Stage<CT, UNROLL> ring[DEPTH];
+    Stage<CT, UNROLL, BITS> ring[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_stage(ring[d], d);
     x_store(tid, xv);
@@ -359,7 +403,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const char *xrow = x_lds + min(col, m - 1) * geo.x_row_bytes;
     const uint32_t *szrow = sz_lds + col * geo.sz_stride;
-    auto compute = [&](const Stage<CT, UNROLL> &st, int i) {
+    auto compute = [&](const Stage<CT, UNROLL, BITS> &st, int i) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = (i * SPLIT + wave) * UNROLL + u;
@@ -375,7 +419,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
             uint32_t sz[CT];
 #pragma unroll
             for (int t = 0; t < CT; ++t) sz[t] = szrow[t * 16 * geo.sz_stride + g];
-            process_block<CT, FOLD>(acc, a, st.w[u], sz, wa.valid(kb));
+            process_block<CT, FOLD, BITS>(acc, a, st.w[u], sz, wa.valid(kb));
         }
     };
 
@@ -402,7 +446,7 @@ struct Coop {
     uint16_t s[SC], z[SC];
 };
 
-template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX>
+template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX, int BITS = 4>
 __global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -429,13 +473,16 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
     const int row0 = blockIdx.x * ROWS;
     const int nwin = (kblocks + WB - 1) / WB;
 
-    WeightAddr<CT> wa;
+    constexpr int LPB = BITS / 4;
+    WeightAddr<CT, BITS> wa;
     wa.init(qweight, x, geo, row0, col, quarter);
-    auto load_weights = [&](Stage<CT, UNROLL> &st, int win) {
+    auto load_weights = [&](Stage<CT, UNROLL, BITS> &st, int win) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-            for (int t = 0; t < CT; ++t) st.w[u][t] = wa.load(win * WB + wave * UNROLL + u, t);
+            for (int t = 0; t < CT; ++t)
+#pragma unroll
+                for (int l = 0; l < LPB; ++l) st.w[u][t * LPB + l] = wa.load(win * WB + wave * UNROLL + u, t, l);
     };
 
     constexpr int MAX_XCHUNKS = MMAX * WB * 4;             // m <= MMAX rows
@@ -473,8 +520,8 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
             const int ch = tid + i * THREADS;
             if (ch < n_xchunks) {
                 const int r = ch / (WB * 4), rem = ch % (WB * 4);     // rem = block * 4 + quarter
-                store_x_chunk(x_lds + buf * x_buf_bytes + r * geo.x_row_bytes + (rem >> 2) * 256, rem & 3,
-                              c.x[i]);
+                store_x_chunk<BITS>(x_lds + buf * x_buf_bytes + r * geo.x_row_bytes + (rem >> 2) * 256, rem & 3,
+                                    c.x[i]);
             }
         }
 #pragma unroll
@@ -492,7 +539,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
 #pragma unroll
     for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int xr = min(col, m - 1);
-    auto compute = [&](const Stage<CT, UNROLL> &st, int win, int buf) {
+    auto compute = [&](const Stage<CT, UNROLL, BITS> &st, int win, int buf) {
         const char *xb = x_lds + buf * x_buf_bytes + xr * geo.x_row_bytes;
         const uint32_t *szb = reinterpret_cast<const uint32_t *>(sz_lds + buf * sz_buf_bytes) + col * geo.sz_stride;
 #pragma unroll
@@ -506,14 +553,14 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
             uint32_t sz[CT];
 #pragma unroll
             for (int t = 0; t < CT; ++t) sz[t] = szb[t * 16 * geo.sz_stride + gw];
-            process_block<CT, FOLD>(acc, a, st.w[u], sz, wa.valid(win * WB + kbl));
+            process_block<CT, FOLD, BITS>(acc, a, st.w[u], sz, wa.valid(win * WB + kbl));
         }
     };
 
     // Two register stages, two LDS buffers; the body is unrolled by two and
     // its loads are unconditional (past the end they are redirected), so the
     // compiler waits only for the older stage.
-    Stage<CT, UNROLL> s0, s1;
+    Stage<CT, UNROLL, BITS> s0, s1;
     Coop<XC, SC> cp;
     coop_load(cp, 0);
     load_weights(s0, 0);
@@ -540,14 +587,14 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_window_kernel(
 // ---------------------------------------------------------------------------
 constexpr size_t kMaxLds = 160 * 1024;     // per workgroup on gfx950
 
-Geometry make_geometry(int m, int n_out, int n_in, int group_shift)
+Geometry make_geometry(int m, int n_out, int n_in, int group_shift, int bits)
 {
     Geometry g;
     g.m = m;
     g.n_out = n_out;
     g.n_in = n_in;
     g.group_shift = group_shift;
-    g.words_per_row = n_in >> 3;
+    g.words_per_row = n_in * bits / 32;
     g.groups_per_row = group_shift >= 31 ? 1 : n_in >> group_shift;   // 31: one group per row
     g.kblocks = (n_in + 127) >> 7;
     g.last_full_quarter = ((n_in - ((g.kblocks - 1) << 7)) >> 5) - 1;
@@ -567,13 +614,13 @@ hipError_t allow_full_lds(K kernel)
     return e;
 }
 
-template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD>
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4>
 bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                    const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
                    uint16_t *y, hipStream_t stream, hipError_t *err)
 {
     static_assert(SPLIT >= CT || SPLIT == 1, "the LDS reduction assigns one wave per tile");
-    Geometry g = make_geometry(m, n_out, n_in, group_shift);
+    Geometry g = make_geometry(m, n_out, n_in, group_shift, BITS);
     g.sz_stride = g.groups_per_row | 1;
     g.x_row_bytes = g.kblocks * 256 + 16;
     g.sz_vector = ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 15) == 0 &&
@@ -582,7 +629,7 @@ bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *s
     const size_t part = SPLIT > 1 ? (size_t)SPLIT * CT * 1024 : 0;
     const size_t lds = (x_bytes > part ? x_bytes : part) + (size_t)16 * CT * g.sz_stride * 4;
     if (lds > kMaxLds) return false;
-    auto kernel = gemv_resident_kernel<SPLIT, CT, UNROLL, DEPTH, FOLD>;
+    auto kernel = gemv_resident_kernel<SPLIT, CT, UNROLL, DEPTH, FOLD, BITS>;
     if (lds > 64 * 1024) {
         const hipError_t e = allow_full_lds(kernel);
         if (e != hipSuccess) {
@@ -597,7 +644,7 @@ bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *s
     return true;
 }
 
-template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX>
+template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX, int BITS = 4>
 bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                  const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
                  uint16_t *y, hipStream_t stream, hipError_t *err)
@@ -606,14 +653,14 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
     static_assert(SPLIT * UNROLL % 2 == 0, "a window must hold whole groups of 256");
     constexpr int WB = SPLIT * UNROLL;
     if (m > MMAX) return false;
-    Geometry g = make_geometry(m, n_out, n_in, group_shift);
+    Geometry g = make_geometry(m, n_out, n_in, group_shift, BITS);
     g.sz_stride = ((WB * 128) >> group_shift) | 1;
     g.x_row_bytes = WB * 256 + 16;
     const size_t x_region = 2 * (size_t)m * g.x_row_bytes;
     const size_t part = SPLIT > 1 ? (size_t)SPLIT * CT * 1024 : 0;
     const size_t lds = (x_region > part ? x_region : part) + 2 * (size_t)16 * CT * g.sz_stride * 4;
     if (lds > kMaxLds) return false;
-    auto kernel = gemv_window_kernel<SPLIT, CT, UNROLL, FOLD, MMAX>;
+    auto kernel = gemv_window_kernel<SPLIT, CT, UNROLL, FOLD, MMAX, BITS>;
     if (lds > 64 * 1024) {
         const hipError_t e = allow_full_lds(kernel);
         if (e != hipSuccess) {
@@ -631,7 +678,7 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 // Configurations chosen from measured sweeps on MI355X over the decode
 // shapes (7B and 70B projections, m = 1 and 8); other shapes fall through to
 // the nearest rule.  Every rule ends in a configuration that always fits.
-template <bool FOLD>
+template <bool FOLD, int BITS>
 hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
                     uint16_t *y, hipStream_t stream)
@@ -640,9 +687,9 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
     const int kblocks = (n_in + 127) >> 7;
     const int tiles = (n_out + 15) / 16;
 #define Q4_RES(S, C, U, D) \
-    if (plan_resident<S, C, U, D, FOLD>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+    if (plan_resident<S, C, U, D, FOLD, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
 #define Q4_WIN(S, C, U, MM) \
-    if (plan_window<S, C, U, FOLD, MM>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+    if (plan_window<S, C, U, FOLD, MM, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
     if (kblocks >= 16) {
         if (!FOLD) {
             if (m == 1) {
@@ -676,19 +723,21 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
 
 hipError_t q4_launch_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, uint16_t *y, hipStream_t stream)
+                          int group_size, int bits, uint16_t *y, hipStream_t stream)
 {
     // group k of a row is k >> shift; a per-channel group of any other
     // length than a power of two uses shift 31 (every k in group 0)
     int shift = 0;
     while ((1 << shift) < group_size) ++shift;
     if ((1 << shift) != group_size) shift = 31;
+    if (bits == 8)
+        return dispatch<false, 8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
     // The fold applies s and z once per 128-wide block after summing raw
     // codes, subtracting z * sum(x) from the code sum; with one scale per
     // row (per-channel) most codes sit at z and that subtraction would
     // cancel terms far larger than the result, so per-channel weights take
     // the exact-subtraction form.
     return (group_size == 128 || group_size == 256)
-               ? dispatch<true>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream)
-               : dispatch<false>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
+               ? dispatch<true, 4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream)
+               : dispatch<false, 4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
 }

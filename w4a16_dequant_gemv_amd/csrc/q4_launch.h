@@ -15,8 +15,8 @@ hipError_t q4_launch_dequant(const uint32_t *qweight, const uint16_t *scales,
 
 hipError_t q4_launch_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, uint16_t *y, hipStream_t stream);
+                          int group_size, int bits, uint16_t *y, hipStream_t stream);
 
 hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, uint16_t *y, hipStream_t stream);
+                          int group_size, int bits, uint16_t *y, hipStream_t stream);
