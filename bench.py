@@ -40,9 +40,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(n_out, n_in, m, g):
+def algorithmic_bytes(n_out, n_in, m, g, bits=4):
     """Bytes the method must move for one linear: codes, s and z, x and y."""
-    return n_out * n_in // 2 + 4 * n_out * (n_in // g) + 2 * m * n_in + 2 * m * n_out
+    return n_out * n_in * bits // 8 + 4 * n_out * (n_in // g) + 2 * m * n_in + 2 * m * n_out
 
 
 def time_graph(graph, steps, warmup):
@@ -284,6 +284,53 @@ def bench_single(args, dev):
                 gbs=round(algorithmic_bytes(n_out, n_in, 1, 128) / t / 1e9, 1))
 
 
+def bench_int8(args, dev):
+    """W8A16: decode at m=1 over 8 layers of the fused 7B linears with INT8
+    per-channel weights (1.7 GB, beyond the Infinity Cache), and prefill at
+    m=2048 on the 7B projection shapes with INT8 g=128 weights."""
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    lin = syn.LLAMA7B_LINEARS
+    fused = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+    xs = {name: syn.activations_f16_device(1, lin[idx[0]].n_in, 2200 + j, dev)
+          for j, (name, idx) in enumerate(fused)}
+    layers, gemvs = 8, []
+    for layer in range(layers):
+        for name, idx in fused:
+            w = torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama7b_seed(layer, i),
+                                                    0.02, syn.n_outliers(lin[i].n_in), dev) for i in idx])
+            qw = w4.quantize_pack(w, None, bits=8)
+            del w
+            gemvs.append((qw, xs[name], torch.empty((1, qw.n_out), dtype=torch.float16, device=dev)))
+    g = capture(lambda: [w4.gemv(x, qw, y) for qw, x, y in gemvs])
+    el, _ = time_graph(g, 10, 2)
+    nbytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 1, qw.n_in, 8) for qw, _, _ in gemvs)
+    res = dict(decode_layers=layers, decode_m=1, decode_group="per-channel",
+               decode_gbs=round(nbytes * 10 / el / 1e9, 1),
+               decode_us_per_launch=round(el / (10 * len(gemvs)) * 1e6, 2))
+    del gemvs, g
+    out, tot_flop, tot_t = [], 0, 0.0
+    for i, pl in enumerate(syn.PREFILL_LINEARS):
+        w = syn.normal_weight_device(pl.n_out, pl.n_in, 4000 + i, 0.02, syn.n_outliers(pl.n_in), dev)
+        qw = w4.quantize_pack(w, 128, bits=8)
+        del w
+        x = syn.activations_f16_device(syn.PREFILL_M, pl.n_in, 4100 + i, dev)
+        y = torch.empty((syn.PREFILL_M, pl.n_out), dtype=torch.float16, device=dev)
+        reps = 20
+        gr = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
+        el, _ = time_graph(gr, 3, 1)
+        t = el / (3 * reps)
+        flop = 2 * syn.PREFILL_M * pl.n_out * pl.n_in
+        out.append(dict(shape=f"{syn.PREFILL_M}x{pl.n_out}x{pl.n_in}", tflops=round(flop / t / 1e12, 1)))
+        tot_flop += flop
+        tot_t += t
+    res["prefill_g128_shapes"] = out
+    res["prefill_g128_tflops"] = round(tot_flop / tot_t / 1e12, 1)
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_stress_and_quantize(args, dev):
     import torch
     import w4a16_dequant_gemv_amd as w4
@@ -383,6 +430,8 @@ def main():
         log(f"stress: {extras['stress']}")
         extras["single"] = bench_single(args, dev)
         log(f"single 4096x4096 GEMV: {extras['single']}")
+        extras["int8"] = bench_int8(args, dev)
+        log(f"int8 (W8A16): {extras['int8']}")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host_w, args.cpu_seconds)
@@ -425,6 +474,7 @@ def main():
         record["decode70b"] = dict(extras["decode70b"], frac=round(extras["decode70b"]["gbs"] / HBM_PEAK_GBS, 4))
         record["stress"] = extras["stress"]
         record["single_gemv_4096x4096"] = extras["single"]
+        record["w8a16"] = extras["int8"]
     print(json.dumps(record), flush=True)
 
 

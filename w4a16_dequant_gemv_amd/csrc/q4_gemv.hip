@@ -676,8 +676,8 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 }
 
 // Configurations chosen from measured sweeps on MI355X over the decode
-// shapes (7B and 70B projections, m = 1 and 8); other shapes fall through to
-// the nearest rule.  Every rule ends in a configuration that always fits.
+// shapes (7B and 70B projections, m = 1 and 8, INT4 and INT8); other shapes
+// fall through to the nearest rule.  Every rule ends in a configuration that always fits.
 template <bool FOLD, int BITS>
 hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
@@ -691,7 +691,17 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
 #define Q4_WIN(S, C, U, MM) \
     if (plan_window<S, C, U, FOLD, MM, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
     if (kblocks >= 16) {
-        if (!FOLD) {
+        if constexpr (BITS == 8) {
+            // twice the bytes per code: fewer waves per tile keep more
+            // workgroups in flight per CU
+            if (m == 1) {
+                if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 2, 2);
+                if (tiles <= 256) Q4_RES(4, 1, 1, 3);
+                Q4_RES(4, 1, 1, 2);
+            }
+            if (m <= 4) Q4_RES(8, 1, 1, 2);
+            Q4_RES(8, 2, 1, 2);
+        } else if (!FOLD) {
             if (m == 1) {
                 if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 1, 3);
                 if (kblocks >= 128 && tiles >= 512) Q4_RES(16, 1, 1, 2);
