@@ -209,8 +209,8 @@ def bench_prefill(args, dev):
         y = torch.empty((syn.PREFILL_M, lin.n_out), dtype=torch.float16, device=dev)
         reps = 20
         g = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
-        el, _ = time_graph(g, 3, 1)
-        t = el / (3 * reps)
+        el, _ = time_graph(g, 5, 3)
+        t = el / (5 * reps)
         flop = 2 * syn.PREFILL_M * lin.n_out * lin.n_in
         out.append(dict(shape=f"{syn.PREFILL_M}x{lin.n_out}x{lin.n_in}", us=round(t * 1e6, 2),
                         tflops=round(flop / t / 1e12, 1)))
@@ -319,8 +319,8 @@ def bench_int8(args, dev):
         y = torch.empty((syn.PREFILL_M, pl.n_out), dtype=torch.float16, device=dev)
         reps = 20
         gr = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
-        el, _ = time_graph(gr, 3, 1)
-        t = el / (3 * reps)
+        el, _ = time_graph(gr, 5, 3)
+        t = el / (5 * reps)
         flop = 2 * syn.PREFILL_M * pl.n_out * pl.n_in
         out.append(dict(shape=f"{syn.PREFILL_M}x{pl.n_out}x{pl.n_in}", tflops=round(flop / t / 1e12, 1)))
         tot_flop += flop

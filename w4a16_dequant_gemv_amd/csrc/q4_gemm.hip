@@ -119,7 +119,11 @@ __device__ __forceinline__ void interleave()
     }
 }
 
-template <int BM, int BN, int WM, int WN, int BITS = 4>
+// PAIR_SZ: the two lanes of each lane pair dequantize slices of the same
+// row and group (every case but INT4 with groups of 32), so the even lane
+// loads the scale, the odd lane the zero-point, and a DPP swap gives each
+// lane both: one 2-byte gather per slice and step instead of two.
+template <int BM, int BN, int WM, int WN, int BITS, bool PAIR_SZ>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -188,6 +192,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(zg), (short)0, rows_n * groups_per_row * 2, kBufferFlags);
     uint32_t xoff[A_CHUNKS], woff[B_SLICES], soff[B_SLICES];
+    const uint16_t *szp[B_SLICES];                      // PAIR_SZ: this lane's scale or zero-point row
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
         const int c = tid + i * THREADS;                   // row c/8, chunk c%8
@@ -200,6 +205,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         const int r = min(c / SPR, n_out - 1 - n0);
         woff[i] = (uint32_t)r * (uint32_t)words_per_row * 4u + (uint32_t)(c % SPR) * 16u;
         soff[i] = ((uint32_t)r * (uint32_t)groups_per_row + (uint32_t)(((c % SPR) * CPS) >> group_shift)) * 2u;
+        szp[i] = reinterpret_cast<const uint16_t *>(((c & 1) ? zg : sg) + soff[i]);
     }
     // LDS byte offsets within a stage: x chunk i of this lane, weight chunk
     // j of slice i, fragment rows.  Rows of chunk i differ by multiples of 16
@@ -214,10 +220,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int frow = lane & 31, fkg = lane >> 5, fswz = swz(frow);
     const uint32_t fa = (wave_m * WT_M + frow) * 128, fb = A_BYTES + (wave_n * WT_N + frow) * 128;
 
+    // Register type of the raw scale/zero bits.  Chosen so that no masking
+    // or packing of the loaded halves is placed at the loop's back edge,
+    // where it would wait for loads issued in the same step.
+    using SzBits = std::conditional_t<PAIR_SZ, uint16_t, uint32_t>;
     struct Regs {
         u32x4 a[A_CHUNKS];
         u32x4 w[B_SLICES];
-        uint32_t s[B_SLICES], z[B_SLICES];
+        SzBits s[B_SLICES], z[B_SLICES];               // raw fp16 bits (PAIR_SZ: z unused)
     };
     struct Frag {
         f16x8 a[TM], b[TN];
@@ -237,9 +247,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 #pragma unroll
         for (int i = 0; i < B_SLICES; ++i) {
             g.w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK * BITS / 8), 0);
-            g.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff[i], gk, 0);
-            g.z[i] = __builtin_amdgcn_raw_buffer_load_b16(zr, soff[i], gk, 0);
+            if constexpr (PAIR_SZ) {
+                g.s[i] = szp[i][gk >> 1];
+            } else {
+                g.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff[i], gk, 0);
+                g.z[i] = __builtin_amdgcn_raw_buffer_load_b16(zr, soff[i], gk, 0);
+            }
         }
+    };
+    // Scale and biased zero-point of slice i (PAIR_SZ: swapped in from the
+    // partner lane).
+    auto scale_bias = [&](const Regs &g, int i, f16x2 &scale, f16x2 &bias) {
+        uint32_t sb, zb;
+        if constexpr (PAIR_SZ) {
+            const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)g.s[i], 0xB1, 0xF, 0xF, false);
+            sb = (tid & 1) ? other : g.s[i];
+            zb = (tid & 1) ? g.s[i] : other;
+        } else {
+            sb = g.s[i];
+            zb = g.z[i];
+        }
+        const _Float16 sv = bitcast<_Float16>((uint16_t)sb);
+        const _Float16 zv = bitcast<_Float16>((uint16_t)zb) + (_Float16)1024.0f;
+        scale = f16x2{sv, sv};
+        bias = f16x2{zv, zv};
     };
     auto load_all = [&](Regs &g, int kt) {
 #pragma unroll
@@ -257,9 +288,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 #pragma unroll
             for (int q = 0; q < B_PART; ++q) {
                 const int wd = p * B_PART + q, i = wd >> 2, j = wd & 3;
-                const _Float16 sv = bitcast<_Float16>((uint16_t)g.s[i]);
-                const _Float16 zb = bitcast<_Float16>((uint16_t)g.z[i]) + (_Float16)1024.0f;
-                const f16x2 scale = {sv, sv}, bias = {zb, zb};
+                f16x2 scale, bias;
+                scale_bias(g, i, scale, bias);
                 *reinterpret_cast<u32x4 *>(smem + buf + b_st[j] + i * B_ROW_STEP) =
                     dequant_word_natural(g.w[i][j], bias, scale);
             }
@@ -268,9 +298,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 #pragma unroll
             for (int q = 0; q < B_PART; q += 2) {
                 const int wd = p * B_PART + q, i = wd >> 2, j = wd & 3;
-                const _Float16 sv = bitcast<_Float16>((uint16_t)g.s[i]);
-                const _Float16 zb = bitcast<_Float16>((uint16_t)g.z[i]) + (_Float16)1024.0f;
-                const f16x2 scale = {sv, sv}, bias = {zb, zb};
+                f16x2 scale, bias;
+                scale_bias(g, i, scale, bias);
                 const u32x2 lo = dequant_byte_word(g.w[i][j], bias, scale);
                 const u32x2 hi = dequant_byte_word(g.w[i][j + 1], bias, scale);
                 *reinterpret_cast<u32x4 *>(smem + buf + b_st[j >> 1] + i * B_ROW_STEP) =
@@ -317,13 +346,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         Regs R[3];
         Frag f0, f1;
         const int kmax = ksteps - 1;
+        // The prologue issues its loads in the loop's own order, pinned by
+        // scheduling barriers, so the wait counts the compiler places at the
+        // loop head stay three steps deep.
         load_all(R[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
         load_all(R[1], min(1, kmax));
+        __builtin_amdgcn_sched_barrier(0);
         load_all(R[2], min(2, kmax));
+        __builtin_amdgcn_sched_barrier(0);
         store_all(R[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
         load_all(R[0], min(3, kmax));
+        __builtin_amdgcn_sched_barrier(0);
         store_all(R[1], STAGE);
+        __builtin_amdgcn_sched_barrier(0);
         load_all(R[1], min(4, kmax));
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         read_frag(f0, 0, 0);
 
@@ -359,7 +398,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
             load_a(g, kl, 3);
             load_b(g, kl);
             mma(f1);
-            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + 3 * B_SLICES, NVALU>();
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + (PAIR_SZ ? 2 : 3) * B_SLICES, NVALU>();
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
         };
@@ -478,14 +517,14 @@ hipError_t allow_lds(K kernel, size_t bytes)
     return e;
 }
 
-template <int BM, int BN, int WM, int WN, int BITS = 4>
+template <int BM, int BN, int WM, int WN, int BITS, bool PAIR_SZ>
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                        const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
                        uint16_t *y, hipStream_t stream)
 {
     const int tiles_m = (m + BM - 1) / BM, tiles_n = (n_out + BN - 1) / BN;
     const size_t lds = kStages * (size_t)(BM + BN) * 128;
-    auto kernel = gemm_kernel<BM, BN, WM, WN, BITS>;
+    auto kernel = gemm_kernel<BM, BN, WM, WN, BITS, PAIR_SZ>;
     const hipError_t e = allow_lds(kernel, lds);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
@@ -506,8 +545,13 @@ hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint
     while ((1 << shift) < group_size) ++shift;
     if ((1 << shift) != group_size) shift = 31;
     if (bits == 8)
-        return launch_gemm<256, 128, 4, 1, 8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
-                                              shift, y, stream);
-    return launch_gemm<256, 128, 4, 1>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift,
-                                       y, stream);
+        return launch_gemm<256, 128, 4, 1, 8, true>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
+                                                    shift, y, stream);
+    // INT4 slices hold 32 codes: with groups of 32 the two slices of a row
+    // step belong to different groups
+    if (group_size == 32)
+        return launch_gemm<256, 128, 4, 1, 4, false>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in,
+                                                     shift, y, stream);
+    return launch_gemm<256, 128, 4, 1, 4, true>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift,
+                                                y, stream);
 }
