@@ -1,5 +1,5 @@
-"""CPU oracle for group-wise (or per-channel) INT4 / INT8 weight quantization
-and the W4A16 / W8A16 linear layer.
+"""CPU oracle for group-wise (or per-channel) INT4 / INT8 weight quantization,
+the W4A16 / W8A16 linear layer and the KV-cache codec.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The GPU library
@@ -7,7 +7,8 @@ never loads it and shares no code with it; the C source `q4_oracle.c` holds
 the arithmetic, and this module only marshals numpy arrays into it.
 
 Every function cites the passage it follows in `q4_oracle.c`.  Parity
-status: the quantizer, dequantizer, fp16 converter and reference product are
+status: the quantizer, dequantizer, fp16 converter, reference product and
+KV codec are
 pinned by the CPU tests (brute force, the worked example of the interview
 guide's §3, closed forms and invariants); the packing order is this
 library's own convention (the pages give none) and is pinned only by the
@@ -49,6 +50,14 @@ class Oracle:
                                                _p, _p, _p, _p]
         lib.orc_dequant_bits.argtypes = [_p, _p, _p, _c_i64, _c_i64, _c_i32, _c_i32, _p]
         lib.orc_linear_ref.argtypes = [_p, _p, _c_i64, _c_i64, _c_i64, _p, _p]
+        lib.orc_kv_quant_tokens.restype = ctypes.c_int
+        lib.orc_kv_quant_tokens.argtypes = [_p, _c_i64, _c_i32, _c_i32, _p, _p]
+        lib.orc_kv_quant_channels.restype = ctypes.c_int
+        lib.orc_kv_quant_channels.argtypes = [_p, _c_i64, _c_i32, _c_i32, _c_i32, _p, _p]
+        lib.orc_kv_dequant_tokens.argtypes = [_p, _p, _c_i64, _c_i32, _p]
+        lib.orc_kv_dequant_channels.argtypes = [_p, _p, _c_i64, _c_i32, _c_i32, _p]
+        lib.orc_kv_cache_bytes.restype = ctypes.c_double
+        lib.orc_kv_cache_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32]
         self.lib = lib
 
     # -- binary32 <-> binary16 ------------------------------------------------
@@ -138,6 +147,69 @@ class Oracle:
     def linear_from_packed(self, x_f16_bits, packed, scales, zeros, group_size, bits=4):
         """Dequantize, then take the reference product (two plain steps)."""
         return self.linear_ref(x_f16_bits, self.dequant(packed, scales, zeros, group_size, bits))
+
+
+    # -- KV-cache codec (q4_oracle.c, "KV-cache codec") -------------------------
+    def kv_quant_tokens(self, x_f16_bits, bits=8):
+        """fp16 bits [..., d] -> (int8 codes [..., d], fp32 scale [...]): one
+        symmetric scale per token row (the V side)."""
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        d = x.shape[-1]
+        rows = x.size // d
+        q = np.empty(x.shape, dtype=np.int8)
+        s = np.empty(x.shape[:-1], dtype=np.float32)
+        rc = self.lib.orc_kv_quant_tokens(x.ctypes.data, rows, d, bits, q.ctypes.data, s.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected kv_quant_tokens d={d} bits={bits}")
+        return q, s
+
+    def kv_quant_channels(self, x_f16_bits, bits=8):
+        """fp16 bits [blocks, t, d] -> (int8 codes [blocks, t, d], fp32 scale
+        [blocks, d]): one symmetric scale per channel of a block (the K side)."""
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        blocks, t, d = x.shape
+        q = np.empty(x.shape, dtype=np.int8)
+        s = np.empty((blocks, d), dtype=np.float32)
+        rc = self.lib.orc_kv_quant_channels(x.ctypes.data, blocks, t, d, bits, q.ctypes.data,
+                                            s.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected kv_quant_channels t={t} d={d} bits={bits}")
+        return q, s
+
+    def kv_dequant_tokens(self, q, s):
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        d = q.shape[-1]
+        out = np.empty(q.shape, dtype=np.uint16)
+        self.lib.orc_kv_dequant_tokens(q.ctypes.data, s.ctypes.data, q.size // d, d, out.ctypes.data)
+        return out
+
+    def kv_dequant_channels(self, q, s):
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        blocks, t, d = q.shape
+        out = np.empty(q.shape, dtype=np.uint16)
+        self.lib.orc_kv_dequant_channels(q.ctypes.data, s.ctypes.data, blocks, t, d, out.ctypes.data)
+        return out
+
+    def kv_flush(self, k_blocks, v_blocks, dst, pool_blocks, bits=8):
+        """Quantize blocks of the FP16 window into a block pool: block p goes to
+        pool slot dst[p] (K per channel, V per token); entries of dst outside
+        [0, pool_blocks) are skipped.  Returns the pool arrays, untouched slots
+        zero."""
+        kq, ks = self.kv_quant_channels(k_blocks, bits)
+        vq, vs = self.kv_quant_tokens(v_blocks, bits)
+        _, t, d = kq.shape
+        pool = dict(k=np.zeros((pool_blocks, t, d), np.int8), k_scale=np.zeros((pool_blocks, d), np.float32),
+                    v=np.zeros((pool_blocks, t, d), np.int8), v_scale=np.zeros((pool_blocks, t), np.float32))
+        for p, slot in enumerate(np.asarray(dst).tolist()):
+            if 0 <= slot < pool_blocks:
+                pool["k"][slot], pool["k_scale"][slot] = kq[p], ks[p]
+                pool["v"][slot], pool["v_scale"][slot] = vq[p], vs[p]
+        return pool
+
+    def kv_cache_bytes(self, layers, kv_heads, head_dim, seq, batch, bits):
+        return self.lib.orc_kv_cache_bytes(layers, kv_heads, head_dim, seq, batch, bits)
 
 
 _DEFAULT = None

@@ -1,6 +1,7 @@
 /*
  * q4_oracle.c -- CPU oracle for group-wise INT4 / INT8 weight quantization
- * (per group or per output channel) and the W4A16 / W8A16 linear layer.
+ * (per group or per output channel), the W4A16 / W8A16 linear layer and the
+ * KV-cache codec (V per token, K per channel, symmetric INT8 / INT4).
  *
  * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct
  * definition that the GPU library is checked against.  Only the tests, the
@@ -316,4 +317,122 @@ void orc_linear_ref(const uint16_t *x_f16, const float *w_deq,
             a[i * n_out + n] = acc_abs;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV-cache codec.                                                           */
+/* [Guide] §6 (KV Cache 量化): K and V are quantized differently -- K per    */
+/* channel (its outliers sit in fixed channels), V per token -- and the      */
+/* most recent tokens (about 128) stay in FP16.  Its quant_kv_per_token      */
+/* listing is the symmetric map with one scale per token over the head       */
+/* dimension: qmax = 2^(b-1) - 1, scale = max|v| / qmax floored at 1e-8,     */
+/* q = clamp(round(v / scale), -qmax - 1, qmax) stored as int8.  [Intro]     */
+/* §3.2 asks for separate scale factors for K and V.                         */
+/* Readings: the cache holds fp16 values, widened exactly to binary32; every */
+/* step is one binary32 operation (the weight quantizer's precision); the    */
+/* scale is kept in binary32; K is quantized per channel over a block of t   */
+/* consecutive tokens of one head (the block that leaves the FP16 window);   */
+/* dequantization is the binary32 product q * scale, rounded once more to    */
+/* fp16 for the cache consumer.  Both quantizers are the symmetric case of   */
+/* orc_quantize_group (pinned above) applied to a token row or to a channel  */
+/* column; pinned by brute force, the [Guide] §3 worked example, the s/2     */
+/* bound, the K/V transposition identity and the [Guide] §6 cache sizes.     */
+/* ------------------------------------------------------------------------ */
+int orc_kv_quant_tokens(const uint16_t *x, int64_t rows, int32_t d, int32_t bits,
+                        int8_t *q, float *scale)
+{
+    if (bits < 2 || bits > 8 || d <= 0)
+        return 1;
+    int failed = 0;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float *v = (float *)malloc((size_t)d * sizeof(float));
+        int32_t *c = (int32_t *)malloc((size_t)d * sizeof(int32_t));
+        if (!v || !c) {
+            #pragma omp atomic write
+            failed = 1;
+            free(v);
+            free(c);
+            continue;
+        }
+        for (int32_t i = 0; i < d; i++)
+            v[i] = orc_f16_to_f32(x[r * d + i]);
+        float s;
+        int32_t z;
+        orc_quantize_group(v, d, bits, 1, &s, &z, c);
+        for (int32_t i = 0; i < d; i++)
+            q[r * d + i] = (int8_t)c[i];
+        scale[r] = s;
+        free(v);
+        free(c);
+    }
+    return failed ? 2 : 0;
+}
+
+/* x [blocks][t][d] -> q [blocks][t][d], scale [blocks][d]: channel j of a
+ * block is quantized over its t tokens. */
+int orc_kv_quant_channels(const uint16_t *x, int64_t blocks, int32_t t, int32_t d,
+                          int32_t bits, int8_t *q, float *scale)
+{
+    if (bits < 2 || bits > 8 || d <= 0 || t <= 0)
+        return 1;
+    int failed = 0;
+    #pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < blocks; b++) {
+        float *v = (float *)malloc((size_t)t * sizeof(float));
+        int32_t *c = (int32_t *)malloc((size_t)t * sizeof(int32_t));
+        if (!v || !c) {
+            #pragma omp atomic write
+            failed = 1;
+            free(v);
+            free(c);
+            continue;
+        }
+        const uint16_t *xb = x + b * (int64_t)t * d;
+        for (int32_t j = 0; j < d; j++) {
+            for (int32_t i = 0; i < t; i++)
+                v[i] = orc_f16_to_f32(xb[(int64_t)i * d + j]);
+            float s;
+            int32_t z;
+            orc_quantize_group(v, t, bits, 1, &s, &z, c);
+            for (int32_t i = 0; i < t; i++)
+                q[b * (int64_t)t * d + (int64_t)i * d + j] = (int8_t)c[i];
+            scale[b * d + j] = s;
+        }
+        free(v);
+        free(c);
+    }
+    return failed ? 2 : 0;
+}
+
+/* Dequantization of per-token rows: out = fp16(q * scale[row]). */
+void orc_kv_dequant_tokens(const int8_t *q, const float *scale, int64_t rows, int32_t d,
+                           uint16_t *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int32_t i = 0; i < d; i++)
+            out[r * d + i] = orc_f32_to_f16((float)q[r * d + i] * scale[r]);
+}
+
+/* Dequantization of per-channel blocks: out = fp16(q * scale[block][channel]). */
+void orc_kv_dequant_channels(const int8_t *q, const float *scale, int64_t blocks, int32_t t,
+                             int32_t d, uint16_t *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < blocks; b++)
+        for (int32_t i = 0; i < t; i++)
+            for (int32_t j = 0; j < d; j++) {
+                const int64_t e = b * (int64_t)t * d + (int64_t)i * d + j;
+                out[e] = orc_f32_to_f16((float)q[e] * scale[b * d + j]);
+            }
+}
+
+/* [Guide] §6: KV cache bytes = 2 (K and V) x layers x kv_heads x head_dim x
+ * seq x batch x bytes per element (codes only, scales not counted). */
+double orc_kv_cache_bytes(int64_t layers, int64_t kv_heads, int64_t head_dim, int64_t seq,
+                          int64_t batch, int32_t bits)
+{
+    return 2.0 * (double)layers * (double)kv_heads * (double)head_dim * (double)seq *
+           (double)batch * (double)bits / 8.0;
 }

@@ -11,7 +11,7 @@ import os
 import numpy as np
 import torch
 
-from brute import check_matrix
+from brute import check_group, check_matrix
 from w4a16_dequant_gemv_amd import synthetic
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -451,10 +451,129 @@ def pin_reconstruction_bound_int8(orc, quick=False):
                                    f"{np.argwhere(bad)[:3].tolist()}")
 
 
+# ---------------------------------------------------------------------------
+# KV-cache codec (the interview guide's §6): V per token, K per channel.
+# ---------------------------------------------------------------------------
+def _kv_cases():
+    """fp16 bit patterns [blocks, t, d] with outlier channels, heavy tails,
+    a zero token and a constant channel."""
+    rng = np.random.default_rng(71)
+    a = rng.standard_normal((3, 16, 32)).astype(np.float32)
+    a[:, :, 5] *= 40.0                              # K-style outlier channel
+    a[1, 3, :] = 0.0                                # an all-zero token
+    a[2, :, 7] = 0.375                              # a constant channel
+    b = (rng.standard_t(3, size=(2, 8, 48)) * 0.3).astype(np.float32)
+    return [a.astype(np.float16).view(np.uint16), b.astype(np.float16).view(np.uint16)]
+
+
+def _check_rows(vals_f32, q, s, bits, where):
+    half = 1 << (bits - 1)
+    for r in range(vals_f32.shape[0]):
+        check_group(vals_f32[r], float(s[r]), half, [int(c) + half for c in q[r]], True,
+                    f"{where} row {r}", bits=bits)
+
+
+def pin_kv_brute_force(orc, quick=False):
+    for ci, x in enumerate(_kv_cases()):
+        xf = _f16_bits_to_f32(x)
+        blocks, t, d = x.shape
+        for bits in (8, 4):
+            q, s = orc.kv_quant_tokens(x, bits)
+            assert q.shape == x.shape and s.shape == (blocks, t)
+            _check_rows(xf.reshape(-1, d), q.reshape(-1, d), s.reshape(-1), bits, f"tokens case {ci} b{bits}")
+            qc, sc = orc.kv_quant_channels(x, bits)
+            assert qc.shape == x.shape and sc.shape == (blocks, d)
+            for b in range(blocks):
+                _check_rows(xf[b].T, qc[b].T, sc[b], bits, f"channels case {ci} block {b} b{bits}")
+
+
+def pin_kv_worked_example(orc, quick=False):
+    """A token whose largest channel is 100: the guide's §3 numbers (scale
+    about 0.787, 0.5 -> 1 -> 0.787) come out of the per-token codec."""
+    g = _golden("worked_example.json")
+    rng = np.random.default_rng(72)
+    row = rng.uniform(-3, 3, size=128).astype(np.float32)
+    row[9] = g["max_abs"]
+    row[40] = g["x"]
+    x = row.astype(np.float16).view(np.uint16)[None, :]
+    q, s = orc.kv_quant_tokens(x, g["bits"])
+    tol = 0.5 * 10.0 ** (-g["scale_printed_digits"])
+    assert abs(float(s[0]) - g["scale_printed"]) <= tol, f"scale {s[0]}"
+    assert int(q[0, 40]) == g["q"] and int(q[0, 9]) == 127
+    x_hat = float(np.float32(q[0, 40]) * s[0])               # the binary32 product
+    assert abs(x_hat - g["x_hat_printed"]) <= tol, f"x_hat {x_hat}"
+    back = orc.kv_dequant_tokens(q, s)                          # then fp16 for the cache consumer
+    assert int(back[0, 40]) == int(np.float16(x_hat).view(np.uint16))
+
+
+def pin_kv_transpose(orc, quick=False):
+    """K per channel over a block equals V per token on the transposed block."""
+    for x in _kv_cases():
+        for bits in (8, 4):
+            qc, sc = orc.kv_quant_channels(x, bits)
+            for b in range(x.shape[0]):
+                qt, st = orc.kv_quant_tokens(np.ascontiguousarray(x[b].T), bits)
+                assert np.array_equal(qc[b], qt.T), f"codes of block {b} differ"
+                assert np.array_equal(sc[b].view(np.uint32), st.view(np.uint32)), f"scales of block {b} differ"
+
+
+def pin_kv_bound(orc, quick=False):
+    """|x - x'| <= s/2 plus the fp16 rounding of x', for both sides."""
+    rng = np.random.default_rng(73)
+    x = (rng.standard_normal((4, 64, 128)) * np.array([1.0] * 120 + [30.0] * 8)).astype(np.float16)
+    xb = x.view(np.uint16)
+    xf = x.astype(np.float64)
+    for bits in (8, 4):
+        q, s = orc.kv_quant_tokens(xb, bits)
+        back = _f16_bits_to_f32(orc.kv_dequant_tokens(q, s)).astype(np.float64)
+        bound = s.astype(np.float64)[..., None] * (0.5 + 2.0 ** -20) + np.abs(back) * 2.0 ** -11
+        assert (np.abs(xf - back) <= bound).all(), f"tokens b{bits}: bound violated"
+        qc, sc = orc.kv_quant_channels(xb, bits)
+        back = _f16_bits_to_f32(orc.kv_dequant_channels(qc, sc)).astype(np.float64)
+        bound = sc.astype(np.float64)[:, None, :] * (0.5 + 2.0 ** -20) + np.abs(back) * 2.0 ** -11
+        assert (np.abs(xf - back) <= bound).all(), f"channels b{bits}: bound violated"
+        # dequantization is the fp32 product, rounded once more to fp16
+        want = (q.astype(np.float32) * s[..., None]).astype(np.float16).view(np.uint16)
+        assert np.array_equal(orc.kv_dequant_tokens(q, s), want)
+
+
+def pin_kv_ties_and_zero(orc, quick=False):
+    # max |v| = 127 gives scale 1 exactly at 8 bits; half-integers round to even
+    vals = [127.0, -126.5, 0.5, 1.5, 2.5, -0.5, -3.5, 5.5, 100.5, -0.0] + [0.0] * 6
+    x = np.array([vals], dtype=np.float16).view(np.uint16)
+    q, s = orc.kv_quant_tokens(x, 8)
+    assert float(s[0]) == 1.0
+    assert q[0].tolist() == [round(v) for v in vals], q[0].tolist()
+    # 4 bits: max |v| = 7 gives scale 1
+    vals4 = [7.0, -6.5, 0.5, 1.5, 2.5, -2.5, 3.5, 0.0]
+    x4 = np.array([vals4], dtype=np.float16).view(np.uint16)
+    q4, s4 = orc.kv_quant_tokens(x4, 4)
+    assert float(s4[0]) == 1.0 and q4[0].tolist() == [round(v) for v in vals4], q4[0].tolist()
+    # an all-zero token: the scale floor, every code 0, zeros back
+    z = np.zeros((1, 64), dtype=np.uint16)
+    qz, sz = orc.kv_quant_tokens(z, 8)
+    assert float(sz[0]) == float(np.float32(1e-8)) and not qz.any()
+    assert not orc.kv_dequant_tokens(qz, sz).any()
+
+
+def pin_kv_cache_sizes(orc, quick=False):
+    g = _golden("kv_cache.json")
+    for e in g["entries"]:
+        gb = orc.kv_cache_bytes(g["layers"], g["kv_heads"], g["head_dim"], g["seq"], g["batch"],
+                                e["bits"]) / 1e9
+        assert abs(gb - e["gb_printed"]) < 1.0, f"{e['bits']}-bit KV cache {gb:.1f} GB vs {e['gb_printed']}"
+    # and the codes the codec writes occupy exactly that many bytes per element
+    x = _kv_cases()[0]
+    q, _ = orc.kv_quant_tokens(x, 8)
+    assert q.nbytes * 2 == x.nbytes
+
+
 ALL_PINS = [
     pin_worked_example, pin_brute_force, pin_ties_to_even, pin_zero_clip,
     pin_reconstruction_bound, pin_idempotence, pin_grid_exact, pin_constant_groups,
     pin_storage_accounting, pin_f16_converter, pin_dequant, pin_linear_ref,
     pin_brute_force_int8_per_channel, pin_ties_to_even_int8, pin_grid_exact_int8,
     pin_dequant_int8, pin_reconstruction_bound_int8,
+    pin_kv_brute_force, pin_kv_worked_example, pin_kv_transpose, pin_kv_bound, pin_kv_ties_and_zero,
+    pin_kv_cache_sizes,
 ]

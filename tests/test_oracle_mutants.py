@@ -45,6 +45,16 @@ MUTANTS = {
                           "(double)orc_f16_to_f32(x_f16[i * n_in + (n_in - 1 - k)])"),
     "linear_abs_dropped": ("acc_abs += fabs(p);", "acc_abs += p;"),
     "linear_row_swap": ("y[i * n_out + n] = acc;", "y[i * n_out + (n_out - 1 - n)] = acc;"),
+    "kv_channel_stride": ("v[i] = orc_f16_to_f32(xb[(int64_t)i * d + j]);",
+                          "v[i] = orc_f16_to_f32(xb[(int64_t)j * t + i]);"),
+    "kv_channel_scale_index": ("scale[b * d + j] = s;", "scale[b * d + (d - 1 - j)] = s;"),
+    "kv_token_asymmetric": ("orc_quantize_group(v, d, bits, 1, &s, &z, c);",
+                            "orc_quantize_group(v, d, bits, 0, &s, &z, c);"),
+    "kv_dequant_channel_scale": ("out[e] = orc_f32_to_f16((float)q[e] * scale[b * d + j]);",
+                                 "out[e] = orc_f32_to_f16((float)q[e] * scale[b * d + i % d]);"),
+    "kv_dequant_double_f16": ("out[r * d + i] = orc_f32_to_f16((float)q[r * d + i] * scale[r]);",
+                              "out[r * d + i] = orc_f32_to_f16((float)q[r * d + i] * orc_f16_to_f32(orc_f32_to_f16(scale[r])));"),
+    "kv_cache_bytes_one_side": ("return 2.0 * (double)layers", "return 1.0 * (double)layers"),
 }
 
 
