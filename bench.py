@@ -15,6 +15,10 @@ Also measured in the same run and reported as extra keys:
   decode70b -- q4_gemv at m=8 over 80 layers of 70B-shaped linears (GB/s),
   stress   -- q4_gemv at m=1 on 8192x28672 for g=128 and g=32 (GB/s),
   quantize -- q4_quantize_pack and q4_dequant on 8192x28672 (GB/s),
+  single_gemv_4096x4096 -- one 4096x4096 linear at m=1 over 64 packed copies,
+  w8a16    -- INT8 decode (8 fused 7B layers, per-channel) and prefill (g=128),
+  kv_codec -- the KV-cache codec on one 70B-shaped layer cache (GB/s) and the
+              decode-time flush of 256 window blocks into a block pool,
   cpu_baseline -- the CPU oracle (dequantize + binary64 product) timed on
                   this host's cores on a bounded sample of the decode step.
 
@@ -59,6 +63,23 @@ def time_graph(graph, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) * 1e-3, wall
+
+
+def time_graph_eager(fn, steps, warmup):
+    """HIP-event time of `steps` eager calls of fn (large kernels: launch cost
+    is negligible next to them)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3, time.perf_counter() - t0
 
 
 def capture(fn):
@@ -331,6 +352,61 @@ def bench_int8(args, dev):
     return res
 
 
+def bench_kv(args, dev):
+    """KV-cache codec on one layer of a Llama-3-70B-shaped cache (batch 32, 8
+    KV heads, 32768 tokens, head dim 128: 2.1 GB of fp16 per side): K
+    quantized per channel over 128-token blocks and V per token (one pass
+    over both), the matching dequantization, and the decode-time flush of one
+    128-token window block per sequence and head (256 blocks) into a pool."""
+    import torch
+    from w4a16_dequant_gemv_amd import kv, synthetic as syn
+    c = syn.KV70B
+    T, D = c["block"], c["head_dim"]
+    blocks = c["batch"] * c["kv_heads"] * c["seq"] // T
+    k = syn.kv_values_device((blocks, T, D), 6200, dev)
+    v = syn.kv_values_device((blocks, T, D), 6201, dev, n_outlier_channels=0)
+    qk, sk = kv.quant_channels(k)
+    qv, sv = kv.quant_tokens(v)
+
+    def quant():
+        kv.quant_channels(k, q=qk, scale=sk)
+        kv.quant_tokens(v, q=qv, scale=sv)
+
+    elems = blocks * T * D
+    q_bytes = 2 * (elems * 2 + elems) + sk.numel() * 4 + sv.numel() * 4
+    quant()
+    el, _ = time_graph_eager(quant, 5, 2)
+    res = dict(cache=f"{c['batch']}x{c['kv_heads']}x{c['seq']}x{D} per side, blocks of {T}",
+               quant_gbs=round(q_bytes * 5 / el / 1e9, 1), quant_ms=round(el / 5 * 1e3, 3))
+    ok, ov = torch.empty_like(k), torch.empty_like(v)
+
+    def deq():
+        kv.dequant_channels(qk, sk, out=ok)
+        kv.dequant_tokens(qv, sv, out=ov)
+
+    deq()
+    el, _ = time_graph_eager(deq, 5, 2)
+    res["dequant_gbs"] = round(q_bytes * 5 / el / 1e9, 1)
+    res["dequant_ms"] = round(el / 5 * 1e3, 3)
+    res["quant_frac"] = round(res["quant_gbs"] / HBM_PEAK_GBS, 4)
+    del ok, ov, qk, qv
+    # decode-time flush: every (sequence, head) hands one full block to the pool
+    P = c["batch"] * c["kv_heads"]
+    pool = kv.KVBlockPool(4 * P, T, D, dev)
+    kb, vb = k[:P].contiguous(), v[:P].contiguous()
+    dst = torch.randperm(4 * P, device=dev)[:P].to(torch.int32)
+    g = capture(lambda: [pool.flush(kb, vb, dst) for _ in range(20)])
+    el, _ = time_graph(g, 5, 2)
+    t_flush = el / (5 * 20)
+    f_bytes = 2 * P * T * D * 2 + 2 * P * T * D + P * (D + T) * 4 + P * 4
+    res["flush_blocks"] = P
+    res["flush_us"] = round(t_flush * 1e6, 2)
+    res["flush_gbs"] = round(f_bytes / t_flush / 1e9, 1)
+    del k, v, kb, vb, pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_stress_and_quantize(args, dev):
     import torch
     import w4a16_dequant_gemv_amd as w4
@@ -432,6 +508,8 @@ def main():
         log(f"single 4096x4096 GEMV: {extras['single']}")
         extras["int8"] = bench_int8(args, dev)
         log(f"int8 (W8A16): {extras['int8']}")
+        extras["kv"] = bench_kv(args, dev)
+        log(f"kv codec: {extras['kv']}")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host_w, args.cpu_seconds)
@@ -475,6 +553,7 @@ def main():
         record["stress"] = extras["stress"]
         record["single_gemv_4096x4096"] = extras["single"]
         record["w8a16"] = extras["int8"]
+        record["kv_codec"] = extras["kv"]
     print(json.dumps(record), flush=True)
 
 

@@ -14,14 +14,18 @@ from w4a16_dequant_gemv_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "kv_codec.h")]
 
 P16 = 0x10000      # 16-byte aligned placeholder address (never dereferenced)
 P2 = 0x10002       # 2-byte but not 16-byte aligned
 
 
 def header_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(q[48]_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = open(h, encoding="utf-8").read()
+        names |= set(re.findall(r"^\s*(?:int|const char \*)\s*((?:q[48]|kv)_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -165,3 +169,66 @@ def test_linear_accepts_per_channel_groups(L, fn):
     f = getattr(L, fn)
     assert f(*_gemv_args(n_in=11008, g=11008, x=None)) == _lib.Q4_ERR_NULL
     assert f(*_gemv_args(n_in=11008, g=11000)) == _lib.Q4_ERR_GROUP
+
+
+def _kv_tok(**kw):
+    a = dict(x=P16, rows=64, d=128, bits=8, q=P16, s=P16)
+    a.update(kw)
+    return (a["x"], a["rows"], a["d"], a["bits"], a["q"], a["s"], None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(x=None), _lib.Q4_ERR_NULL), (dict(q=None), _lib.Q4_ERR_NULL), (dict(s=None), _lib.Q4_ERR_NULL),
+    (dict(rows=0), _lib.Q4_ERR_SHAPE), (dict(d=0), _lib.Q4_ERR_SHAPE), (dict(d=100), _lib.Q4_ERR_SHAPE),
+    (dict(d=520), _lib.Q4_ERR_SHAPE), (dict(bits=6), _lib.Q4_ERR_SHAPE), (dict(bits=16), _lib.Q4_ERR_SHAPE),
+    (dict(x=P16 + 8), _lib.Q4_ERR_ALIGN), (dict(q=P16 + 8), _lib.Q4_ERR_ALIGN), (dict(s=P16 + 2), _lib.Q4_ERR_ALIGN),
+])
+def test_kv_quant_tokens_rejects(L, bad, code):
+    assert L.kv_quant_tokens(*_kv_tok(**bad)) == code
+
+
+def _kv_ch(**kw):
+    a = dict(x=P16, blocks=4, t=128, d=128, bits=8, q=P16, s=P16)
+    a.update(kw)
+    return (a["x"], a["blocks"], a["t"], a["d"], a["bits"], a["q"], a["s"], None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(x=None), _lib.Q4_ERR_NULL), (dict(blocks=0), _lib.Q4_ERR_SHAPE), (dict(t=0), _lib.Q4_ERR_SHAPE),
+    (dict(t=513), _lib.Q4_ERR_SHAPE),               # beyond 32 rows per thread at d = 128
+    (dict(d=256, t=257), _lib.Q4_ERR_SHAPE), (dict(d=12), _lib.Q4_ERR_SHAPE), (dict(bits=3), _lib.Q4_ERR_SHAPE),
+    (dict(x=P16 + 2), _lib.Q4_ERR_ALIGN), (dict(s=P16 + 1), _lib.Q4_ERR_ALIGN),
+])
+def test_kv_quant_channels_rejects(L, bad, code):
+    assert L.kv_quant_channels(*_kv_ch(**bad)) == code
+
+
+def test_kv_limits_accept_the_extremes(L):
+    # the largest t at each d passes the shape rules (the null output is the first error)
+    for d, t in ((8, 8192), (64, 1024), (128, 512), (256, 256), (512, 128)):
+        assert L.kv_quant_channels(*_kv_ch(d=d, t=t, q=None)) == _lib.Q4_ERR_NULL
+        assert L.kv_quant_channels(*_kv_ch(d=d, t=t + 1, q=None)) == _lib.Q4_ERR_NULL
+        assert L.kv_quant_channels(*_kv_ch(d=d, t=t + 1)) == _lib.Q4_ERR_SHAPE
+
+
+def test_kv_dequant_rejects(L):
+    assert L.kv_dequant_tokens(None, P16, 4, 128, P16, None) == _lib.Q4_ERR_NULL
+    assert L.kv_dequant_tokens(P16, P16, 4, 132, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.kv_dequant_tokens(P16, P16, 4, 128, P16 + 2, None) == _lib.Q4_ERR_ALIGN
+    assert L.kv_dequant_channels(P16, P16, 4, 128, 128, None, None) == _lib.Q4_ERR_NULL
+    assert L.kv_dequant_channels(P16, P16 + 4, 4, 128, 128, P16, None) == _lib.Q4_ERR_ALIGN
+    assert L.kv_dequant_channels(P16, P16, 4, 0, 128, P16, None) == _lib.Q4_ERR_SHAPE
+
+
+def test_kv_flush_rejects(L):
+    def call(**kw):
+        a = dict(k=P16, v=P16, blocks=4, t=128, d=128, bits=8, dst=P16, pool=16, kp=P16, ks=P16, vp=P16, vs=P16)
+        a.update(kw)
+        return L.kv_flush_blocks(a["k"], a["v"], a["blocks"], a["t"], a["d"], a["bits"], a["dst"], a["pool"],
+                                 a["kp"], a["ks"], a["vp"], a["vs"], None)
+    assert call(dst=None) == _lib.Q4_ERR_NULL
+    assert call(vs=None) == _lib.Q4_ERR_NULL
+    assert call(pool=0) == _lib.Q4_ERR_SHAPE
+    assert call(bits=5) == _lib.Q4_ERR_SHAPE
+    assert call(dst=P16 + 2) == _lib.Q4_ERR_ALIGN
+    assert call(vp=P16 + 4) == _lib.Q4_ERR_ALIGN

@@ -25,6 +25,11 @@ SIGNATURES = {
     "q8_dequant": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p]),
     "q8_gemv": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
     "q8_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
+    "kv_quant_tokens": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p]),
+    "kv_quant_channels": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p]),
+    "kv_dequant_tokens": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
+    "kv_dequant_channels": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _p, _p]),
+    "kv_flush_blocks": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _p, _p, _p, _p]),
 }
 
 

@@ -3,9 +3,9 @@
     python -m w4a16_dequant_gemv_amd.build
 
 Every translation unit is compiled with packed-fp32 instruction selection
-disabled; the quantizer's unit additionally keeps each fp32 operation
-separate (no FMA contraction) and uses correctly rounded fp32 division, which
-its bit-exactness depends on.
+disabled; the weight quantizer's and the KV codec's units additionally keep
+each fp32 operation separate (no FMA contraction) and use correctly rounded
+fp32 division, which their bit-exactness depends on.
 """
 import os
 import subprocess
@@ -25,11 +25,12 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+EXACT_FP32 = ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math"]
 PER_FILE = {
-    "q4_quantize.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
-                        "-fno-fast-math"],
+    "q4_quantize.hip": EXACT_FP32,
+    "kv_codec.hip": EXACT_FP32,
 }
-SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip"]
+SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip", "kv_codec.hip"]
 
 
 def _compile(src):

@@ -1,6 +1,7 @@
 // q4_api.hip -- the C ABI declared in include/w4a16.h: argument validation
 // (before any HIP call), then one launch on the caller's stream.
 #include "w4a16.h"
+#include "kv_codec.h"
 
 #include "q4_launch.h"
 
@@ -54,6 +55,27 @@ int check_linear(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
     if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 2) ||
         !aligned(y, 2))
         return Q4_ERR_ALIGN;
+    return Q4_OK;
+}
+
+// KV codec shapes: head dimension d a multiple of 8 in [8, 512]; per-channel
+// blocks of t tokens fit 32 rows per thread (t <= 32 * (2048 / d)).
+int check_kv_bits(int32_t bits) { return (bits == 4 || bits == 8) ? Q4_OK : Q4_ERR_SHAPE; }
+
+int check_kv_d(int32_t d) { return (d >= 8 && d <= 512 && d % 8 == 0) ? Q4_OK : Q4_ERR_SHAPE; }
+
+int check_kv_block(int64_t blocks, int32_t t, int32_t d)
+{
+    if (int rc = check_kv_d(d)) return rc;
+    if (blocks <= 0 || blocks > kMaxRows || t <= 0 || t > 32 * (2048 / d)) return Q4_ERR_SHAPE;
+    if (blocks * t * d > kMaxElems) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+int check_kv_rows(int64_t rows, int32_t d)
+{
+    if (int rc = check_kv_d(d)) return rc;
+    if (rows <= 0 || rows * d > kMaxElems) return Q4_ERR_SHAPE;
     return Q4_OK;
 }
 
@@ -176,6 +198,59 @@ int q8_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
         return rc;
     return finish(q4_launch_gemm(x, qweight, scales, zeros, m, n_out, n_in, group_size, 8, y,
                                  (hipStream_t)stream));
+}
+
+int kv_quant_tokens(const uint16_t *x, int64_t rows, int32_t d, int32_t bits, int8_t *q, float *scale,
+                    void *stream)
+{
+    if (!x || !q || !scale) return Q4_ERR_NULL;
+    if (int rc = check_kv_rows(rows, d)) return rc;
+    if (int rc = check_kv_bits(bits)) return rc;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return Q4_ERR_ALIGN;
+    return finish(kv_launch_quant_tokens(x, rows, d, bits, q, scale, (hipStream_t)stream));
+}
+
+int kv_quant_channels(const uint16_t *x, int64_t blocks, int32_t t, int32_t d, int32_t bits, int8_t *q,
+                      float *scale, void *stream)
+{
+    if (!x || !q || !scale) return Q4_ERR_NULL;
+    if (int rc = check_kv_block(blocks, t, d)) return rc;
+    if (int rc = check_kv_bits(bits)) return rc;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return Q4_ERR_ALIGN;
+    return finish(kv_launch_quant_channels(x, blocks, t, d, bits, q, scale, (hipStream_t)stream));
+}
+
+int kv_dequant_tokens(const int8_t *q, const float *scale, int64_t rows, int32_t d, uint16_t *out,
+                      void *stream)
+{
+    if (!q || !scale || !out) return Q4_ERR_NULL;
+    if (int rc = check_kv_rows(rows, d)) return rc;
+    if (!aligned(q, 16) || !aligned(scale, 4) || !aligned(out, 16)) return Q4_ERR_ALIGN;
+    return finish(kv_launch_dequant_tokens(q, scale, rows, d, out, (hipStream_t)stream));
+}
+
+int kv_dequant_channels(const int8_t *q, const float *scale, int64_t blocks, int32_t t, int32_t d,
+                        uint16_t *out, void *stream)
+{
+    if (!q || !scale || !out) return Q4_ERR_NULL;
+    if (int rc = check_kv_block(blocks, t, d)) return rc;
+    if (!aligned(q, 16) || !aligned(scale, 16) || !aligned(out, 16)) return Q4_ERR_ALIGN;
+    return finish(kv_launch_dequant_channels(q, scale, blocks, t, d, out, (hipStream_t)stream));
+}
+
+int kv_flush_blocks(const uint16_t *k, const uint16_t *v, int64_t blocks, int32_t t, int32_t d,
+                    int32_t bits, const int32_t *dst, int64_t pool_blocks, int8_t *k_pool,
+                    float *k_scale, int8_t *v_pool, float *v_scale, void *stream)
+{
+    if (!k || !v || !dst || !k_pool || !k_scale || !v_pool || !v_scale) return Q4_ERR_NULL;
+    if (int rc = check_kv_block(blocks, t, d)) return rc;
+    if (int rc = check_kv_bits(bits)) return rc;
+    if (pool_blocks <= 0 || pool_blocks > kMaxRows || pool_blocks * t * d > kMaxElems) return Q4_ERR_SHAPE;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(dst, 4) || !aligned(k_pool, 16) ||
+        !aligned(k_scale, 4) || !aligned(v_pool, 16) || !aligned(v_scale, 4))
+        return Q4_ERR_ALIGN;
+    return finish(kv_launch_flush(k, v, blocks, t, d, bits, dst, pool_blocks, k_pool, k_scale, v_pool,
+                                  v_scale, (hipStream_t)stream));
 }
 
 }  // extern "C"

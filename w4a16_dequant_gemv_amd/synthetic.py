@@ -89,6 +89,20 @@ def activations_f16_device(m, n_in, seed, device):
                        dtype=torch.float32).half()
 
 
+def kv_values_device(shape, seed, device, n_outlier_channels=4, outlier_scale=20.0):
+    """fp16 cache values [..., d] ~ N(0, 1) on the GPU with n_outlier_channels
+    fixed channels (the same in every token) scaled by outlier_scale: the
+    channel-wise outliers that keys carry."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    d = shape[-1]
+    chans = _rng(seed).choice(d, size=min(n_outlier_channels, d), replace=False)
+    x[..., torch.from_numpy(np.sort(chans)).to(device)] *= outlier_scale
+    return x.half()
+
+
 # ---------------------------------------------------------------------------
 # Workload shapes.
 # ---------------------------------------------------------------------------
@@ -133,3 +147,9 @@ def llama70b_seed(layer, index):
 def n_outliers(n_in):
     """About 0.1 % of the input columns."""
     return int(round(0.001 * n_in))
+
+# KV cache of one Llama-3-70B-shaped layer (80 layers, 8 KV heads of 128 under
+# grouped-query attention) at batch 32 and 32768 tokens; blocks of 128 tokens
+# leave the FP16 window together.
+KV70B = dict(batch=32, kv_heads=8, seq=32768, head_dim=128, block=128, layers=80)
+
