@@ -34,9 +34,18 @@ __device__ __forceinline__ float kv_scale(float amax, float qmax)
     return s < 1e-8f ? 1e-8f : s;
 }
 
-__device__ __forceinline__ uint32_t kv_code(float v, float s, float qmax)
+// round(v / s) clamped to [-qmax - 1, qmax], as the byte of an int8.  The
+// product with r, the hardware reciprocal of s (within 1 ulp), is within
+// 2^-21.5 * |v / s| of the correctly rounded quotient; for |v / s| < 2^7 that
+// is below 2^-14, so both round to the same integer unless the product lies
+// within 2^-14 of a half-integer.  There, and for larger quotients, the
+// correctly rounded division decides: the code is the one round(v / s)
+// gives, bit for bit.
+__device__ __forceinline__ uint32_t kv_code(float v, float s, float r, float qmax)
 {
-    float c = __builtin_rintf(v / s);
+    const float a = v * r;
+    float c = __builtin_rintf(a);
+    if (fabsf(a - c) > 0.5f - 0x1p-14f || fabsf(a) >= 128.0f) c = __builtin_rintf(v / s);
     c = fminf(fmaxf(c, -qmax - 1.0f), qmax);
     return (uint32_t)(int32_t)c & 0xFFu;
 }
@@ -47,46 +56,59 @@ __device__ __forceinline__ void widen8(const u32x4 &raw, float v[8])
     for (int e = 0; e < 8; ++e) v[e] = half_bits_to_float((uint16_t)(raw[e >> 1] >> (16 * (e & 1))));
 }
 
-// Eight codes of one token row against the row's scale.
-__device__ __forceinline__ u32x2 codes8(const float v[8], float s, float qmax)
+// Eight codes of one token row against the row's scale s (reciprocal r).
+__device__ __forceinline__ u32x2 codes8(const float v[8], float s, float r, float qmax)
 {
     u32x2 w = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e >> 2] |= kv_code(v[e], s, qmax) << (8 * (e & 3));
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= kv_code(v[e], s, r, qmax) << (8 * (e & 3));
     return w;
 }
 
 // Eight codes of one chunk against eight channel scales.
-__device__ __forceinline__ u32x2 codes8(const float v[8], const float s[8], float qmax)
+__device__ __forceinline__ u32x2 codes8(const float v[8], const float s[8], const float r[8], float qmax)
 {
     u32x2 w = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e >> 2] |= kv_code(v[e], s[e], qmax) << (8 * (e & 3));
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= kv_code(v[e], s[e], r[e], qmax) << (8 * (e & 3));
     return w;
 }
 
-// Per-token quantization of rows [r_begin, r_end) (stride r_step per pass of
-// the workgroup): LPR lanes per row, lanes past d/8 hold zeros.
-template <int LPR>
+// Per-token quantization of rows r_first + k * r_step < r_end: LPR lanes per
+// row, lanes past d/8 hold zeros.  Each pass handles U rows per lane, their
+// loads issued together so that U * 16 bytes per lane are in flight.
+template <int LPR, int U>
 __device__ __forceinline__ void quant_rows(const uint16_t *__restrict__ x, int64_t r_first, int64_t r_end,
                                            int64_t r_step, int d, float qmax, int8_t *__restrict__ q,
                                            float *__restrict__ scale)
 {
     const int li = threadIdx.x % LPR;
     const bool active = li < d / 8;
-    for (int64_t r = r_first + threadIdx.x / LPR; r < r_end; r += r_step) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (active) raw = *reinterpret_cast<const u32x4 *>(x + r * d + li * 8);
-        float v[8];
-        widen8(raw, v);
-        float a = 0.0f;
+    for (int64_t r = r_first + threadIdx.x / LPR; r < r_end; r += U * r_step) {
+        u32x4 raw[U];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+        for (int u = 0; u < U; ++u) {
+            const int64_t ru = r + u * r_step;
+            raw[u] = u32x4{0u, 0u, 0u, 0u};
+            if (active && ru < r_end) raw[u] = *reinterpret_cast<const u32x4 *>(x + ru * d + li * 8);
+        }
 #pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-        const float s = kv_scale(a, qmax);
-        if (active) *reinterpret_cast<u32x2 *>(q + r * d + li * 8) = codes8(v, s, qmax);
-        if (li == 0) scale[r] = s;
+        for (int u = 0; u < U; ++u) {
+            const int64_t ru = r + u * r_step;
+            float v[8];
+            widen8(raw[u], v);
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+#pragma unroll
+            for (int off = 1; off < LPR; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+            const float s = kv_scale(a, qmax);
+            const float rc = __builtin_amdgcn_rcpf(s);
+            if (ru < r_end) {
+                if (active) *reinterpret_cast<u32x2 *>(q + ru * d + li * 8) = codes8(v, s, rc, qmax);
+                if (li == 0) scale[ru] = s;
+            }
+        }
     }
 }
 
@@ -128,16 +150,19 @@ __device__ __forceinline__ void quant_block_channels(const uint16_t *__restrict_
         scale[j] = s;
     }
     __syncthreads();
-    float s8[8];
+    float s8[8], r8[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s8[e] = chan_scale[c * 8 + e];
+    for (int e = 0; e < 8; ++e) {
+        s8[e] = chan_scale[c * 8 + e];
+        r8[e] = __builtin_amdgcn_rcpf(s8[e]);
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = r0 + i * rs;
         if (act && r < t) {
             float v[8];
             widen8(reg[i], v);
-            *reinterpret_cast<u32x2 *>(q + (int64_t)r * d + c * 8) = codes8(v, s8, qmax);
+            *reinterpret_cast<u32x2 *>(q + (int64_t)r * d + c * 8) = codes8(v, s8, r8, qmax);
         }
     }
 }
@@ -148,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void kv_quant_tokens_kernel(const uint16_
                                                                   float *__restrict__ scale)
 {
     constexpr int RPW = kThreads / LPR;
-    quant_rows<LPR>(x, (int64_t)blockIdx.x * RPW, rows, (int64_t)gridDim.x * RPW, d, qmax, q, scale);
+    quant_rows<LPR, 4>(x, (int64_t)blockIdx.x * RPW, rows, (int64_t)gridDim.x * RPW, d, qmax, q, scale);
 }
 
 // LDS of the per-channel reduction: partial maxima [rows per pass][d] and the
@@ -183,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void kv_flush_kernel(const uint16_t *__re
     if (slot < 0 || slot >= pool_blocks) return;           // uniform across the workgroup
     const int64_t e0 = p * t * d, o0 = slot * t * d;
     quant_block_channels<RPT>(k + e0, t, d, qmax, k_pool + o0, k_scale + slot * d, lds.part, lds.chan_scale);
-    quant_rows<LPR>(v + e0, 0, t, kThreads / LPR, d, qmax, v_pool + o0, v_scale + slot * t);
+    quant_rows<LPR, 2>(v + e0, 0, t, kThreads / LPR, d, qmax, v_pool + o0, v_scale + slot * t);
 }
 
 // Dequantization, eight elements per thread: out = fp16(q * scale).
@@ -205,13 +230,28 @@ __global__ __launch_bounds__(kThreads) void kv_dequant_tokens_kernel(const int8_
                                                                     int d, uint16_t *__restrict__ out)
 {
     const int cpr = d / 8;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * kThreads) {
-        const float s = scale[i / cpr];
-        float s8[8];
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < chunks; i0 += 4 * stride) {
+        u32x2 w[4];
+        float s[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s8[e] = s;
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(q + i * 8);
-        *reinterpret_cast<u32x4 *>(out + i * 8) = dequant8(w, s8);
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * stride;
+            w[u] = u32x2{0u, 0u};
+            s[u] = 0.0f;
+            if (i < chunks) {
+                w[u] = *reinterpret_cast<const u32x2 *>(q + i * 8);
+                s[u] = scale[i / cpr];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * stride;
+            float s8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s8[e] = s[u];
+            if (i < chunks) *reinterpret_cast<u32x4 *>(out + i * 8) = dequant8(w[u], s8);
+        }
     }
 }
 
@@ -221,14 +261,28 @@ __global__ __launch_bounds__(kThreads) void kv_dequant_channels_kernel(const int
 {
     const int cpr = d / 8;
     const int64_t cpb = (int64_t)t * cpr;                  // chunks per block
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * kThreads) {
-        const int64_t b = i / cpb;
-        const int c = (int)(i % cpr);
-        const float *sp = scale + b * d + c * 8;
-        const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp), hi = *reinterpret_cast<const f32x4 *>(sp + 4);
-        const float s8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(q + i * 8);
-        *reinterpret_cast<u32x4 *>(out + i * 8) = dequant8(w, s8);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < chunks; i0 += 4 * stride) {
+        u32x2 w[4];
+        f32x4 lo[4], hi[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * stride;
+            w[u] = u32x2{0u, 0u};
+            lo[u] = hi[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (i < chunks) {
+                const float *sp = scale + (i / cpb) * d + (int)(i % cpr) * 8;
+                w[u] = *reinterpret_cast<const u32x2 *>(q + i * 8);
+                lo[u] = *reinterpret_cast<const f32x4 *>(sp);
+                hi[u] = *reinterpret_cast<const f32x4 *>(sp + 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * stride;
+            const float s8[8] = {lo[u][0], lo[u][1], lo[u][2], lo[u][3], hi[u][0], hi[u][1], hi[u][2], hi[u][3]};
+            if (i < chunks) *reinterpret_cast<u32x4 *>(out + i * 8) = dequant8(w[u], s8);
+        }
     }
 }
 
@@ -260,7 +314,9 @@ template <int LPR>
 hipError_t launch_tokens(const uint16_t *x, int64_t rows, int d, float qmax, int8_t *q, float *scale,
                          hipStream_t stream)
 {
-    kv_quant_tokens_kernel<LPR><<<grid_for(rows, kThreads / LPR), kThreads, 0, stream>>>(x, rows, d, qmax, q, scale);
+    // four rows per lane per pass (quant_rows<LPR, 4>)
+    kv_quant_tokens_kernel<LPR><<<grid_for(rows, 4 * (kThreads / LPR)), kThreads, 0, stream>>>(x, rows, d, qmax, q,
+                                                                                                scale);
     return hipGetLastError();
 }
 
@@ -353,7 +409,7 @@ hipError_t kv_launch_dequant_tokens(const int8_t *q, const float *scale, int64_t
                                     hipStream_t stream)
 {
     const int64_t chunks = rows * (d / 8);
-    kv_dequant_tokens_kernel<<<grid_for(chunks, kThreads), kThreads, 0, stream>>>(q, scale, chunks, d, out);
+    kv_dequant_tokens_kernel<<<grid_for(chunks, 4 * kThreads), kThreads, 0, stream>>>(q, scale, chunks, d, out);
     return hipGetLastError();
 }
 
@@ -361,6 +417,7 @@ hipError_t kv_launch_dequant_channels(const int8_t *q, const float *scale, int64
                                       uint16_t *out, hipStream_t stream)
 {
     const int64_t chunks = blocks * t * (d / 8);
-    kv_dequant_channels_kernel<<<grid_for(chunks, kThreads), kThreads, 0, stream>>>(q, scale, chunks, t, d, out);
+    kv_dequant_channels_kernel<<<grid_for(chunks, 4 * kThreads), kThreads, 0, stream>>>(q, scale, chunks, t, d,
+                                                                                          out);
     return hipGetLastError();
 }
