@@ -1,5 +1,5 @@
 """CPU oracle for group-wise (or per-channel) INT4 / INT8 weight quantization,
-the W4A16 / W8A16 linear layer and the KV-cache codec.
+the W4A16 / W8A16 linear layer, the KV-cache codec and W8A8 with SmoothQuant.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The GPU library
@@ -7,8 +7,8 @@ never loads it and shares no code with it; the C source `q4_oracle.c` holds
 the arithmetic, and this module only marshals numpy arrays into it.
 
 Every function cites the passage it follows in `q4_oracle.c`.  Parity
-status: the quantizer, dequantizer, fp16 converter, reference product and
-KV codec are
+status: the quantizer, dequantizer, fp16 converter, reference product, KV
+codec and W8A8 path are
 pinned by the CPU tests (brute force, the worked example of the interview
 guide's §3, closed forms and invariants); the packing order is this
 library's own convention (the pages give none) and is pinned only by the
@@ -56,6 +56,14 @@ class Oracle:
         lib.orc_kv_quant_channels.argtypes = [_p, _c_i64, _c_i32, _c_i32, _c_i32, _p, _p]
         lib.orc_kv_dequant_tokens.argtypes = [_p, _p, _c_i64, _c_i32, _p]
         lib.orc_kv_dequant_channels.argtypes = [_p, _p, _c_i64, _c_i32, _c_i32, _p]
+        lib.orc_col_absmax_f16.argtypes = [_p, _c_i64, _c_i64, _p]
+        lib.orc_col_absmax_f32.argtypes = [_p, _c_i64, _c_i64, _p]
+        lib.orc_smooth_factors.argtypes = [_p, _p, _c_i64, ctypes.c_float, _p]
+        lib.orc_w8a8_quant_weight.restype = ctypes.c_int
+        lib.orc_w8a8_quant_weight.argtypes = [_p, _p, _c_i64, _c_i64, _p, _p]
+        lib.orc_w8a8_quant_act.restype = ctypes.c_int
+        lib.orc_w8a8_quant_act.argtypes = [_p, _p, _c_i64, _c_i64, _p, _p]
+        lib.orc_w8a8_gemm.argtypes = [_p, _p, _p, _p, _c_i64, _c_i64, _c_i64, _p, _p]
         lib.orc_kv_cache_bytes.restype = ctypes.c_double
         lib.orc_kv_cache_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32]
         self.lib = lib
@@ -210,6 +218,68 @@ class Oracle:
 
     def kv_cache_bytes(self, layers, kv_heads, head_dim, seq, batch, bits):
         return self.lib.orc_kv_cache_bytes(layers, kv_heads, head_dim, seq, batch, bits)
+
+    # -- W8A8 with SmoothQuant (q4_oracle.c, "W8A8 with SmoothQuant") ---------
+    def col_absmax_f16(self, x_f16_bits):
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        out = np.empty(x.shape[1], dtype=np.float32)
+        self.lib.orc_col_absmax_f16(x.ctypes.data, x.shape[0], x.shape[1], out.ctypes.data)
+        return out
+
+    def col_absmax_f32(self, w):
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        out = np.empty(w.shape[1], dtype=np.float32)
+        self.lib.orc_col_absmax_f32(w.ctypes.data, w.shape[0], w.shape[1], out.ctypes.data)
+        return out
+
+    def smooth_factors(self, act_max, w_max, alpha=0.5):
+        """Per input channel s_j = max|X_j|^alpha / max|W_j|^(1-alpha), clamps at 1e-5."""
+        a = np.ascontiguousarray(act_max, dtype=np.float32)
+        w = np.ascontiguousarray(w_max, dtype=np.float32)
+        s = np.empty(a.size, dtype=np.float32)
+        self.lib.orc_smooth_factors(a.ctypes.data, w.ctypes.data, a.size, np.float32(alpha), s.ctypes.data)
+        return s
+
+    def w8a8_quant_weight(self, w, s=None):
+        """W fp32 [n_out][n_in] (times diag(s) if given) -> (int8 [n_out][n_in], fp32 sw [n_out])."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        n_out, n_in = w.shape
+        q = np.empty((n_out, n_in), dtype=np.int8)
+        sw = np.empty(n_out, dtype=np.float32)
+        sp = None if s is None else np.ascontiguousarray(s, dtype=np.float32)
+        rc = self.lib.orc_w8a8_quant_weight(w.ctypes.data, None if sp is None else sp.ctypes.data,
+                                            n_out, n_in, q.ctypes.data, sw.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle w8a8_quant_weight failed")
+        return q, sw
+
+    def w8a8_quant_act(self, x_f16_bits, s=None):
+        """x fp16 bits [m][k] (divided by s if given) -> (int8 [m][k], fp32 sx [m])."""
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        m, k = x.shape
+        q = np.empty((m, k), dtype=np.int8)
+        sx = np.empty(m, dtype=np.float32)
+        sp = None if s is None else np.ascontiguousarray(s, dtype=np.float32)
+        rc = self.lib.orc_w8a8_quant_act(x.ctypes.data, None if sp is None else sp.ctypes.data, m, k,
+                                         q.ctypes.data, sx.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle w8a8_quant_act failed")
+        return q, sx
+
+    def w8a8_gemm(self, qx, sx, qw, sw):
+        """-> (y fp16 bits [m][n], int64 accumulators [m][n])."""
+        qx = np.ascontiguousarray(qx, dtype=np.int8)
+        qw = np.ascontiguousarray(qw, dtype=np.int8)
+        sx = np.ascontiguousarray(sx, dtype=np.float32)
+        sw = np.ascontiguousarray(sw, dtype=np.float32)
+        m, k = qx.shape
+        n = qw.shape[0]
+        assert qw.shape[1] == k
+        acc = np.empty((m, n), dtype=np.int64)
+        y = np.empty((m, n), dtype=np.uint16)
+        self.lib.orc_w8a8_gemm(qx.ctypes.data, sx.ctypes.data, qw.ctypes.data, sw.ctypes.data, m, n, k,
+                               acc.ctypes.data, y.ctypes.data)
+        return y, acc
 
 
 _DEFAULT = None

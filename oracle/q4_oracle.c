@@ -1,7 +1,8 @@
 /*
  * q4_oracle.c -- CPU oracle for group-wise INT4 / INT8 weight quantization
- * (per group or per output channel), the W4A16 / W8A16 linear layer and the
- * KV-cache codec (V per token, K per channel, symmetric INT8 / INT4).
+ * (per group or per output channel), the W4A16 / W8A16 linear layer, the
+ * KV-cache codec (V per token, K per channel, symmetric INT8 / INT4) and the
+ * W8A8 linear layer with SmoothQuant.
  *
  * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct
  * definition that the GPU library is checked against.  Only the tests, the
@@ -435,4 +436,143 @@ double orc_kv_cache_bytes(int64_t layers, int64_t kv_heads, int64_t head_dim, in
 {
     return 2.0 * (double)layers * (double)kv_heads * (double)head_dim * (double)seq *
            (double)batch * (double)bits / 8.0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 with SmoothQuant.                                                    */
+/* [Guide] §4.2 (SmoothQuant): Y = (X diag(s)^-1)(diag(s) W) with per input  */
+/* channel s_j = max|X_j|^alpha / max|W_j|^(1 - alpha), alpha = 0.5 the      */
+/* practical optimum; its smooth_ln_linear listing takes max|W_j| over all   */
+/* linears sharing the input, clamps it and s at 1e-5, multiplies the       */
+/* weights by s and divides the activations (folded into the LayerNorm).     */
+/* W8A8 = INT8 weights and activations on INT8 matrix units ([Guide] §2.3,   */
+/* §4.2); INT8 weights per output channel ([Guide] §2.2); activations        */
+/* quantized per token at run time, the per-token symmetric map of the      */
+/* [Guide] §6 listing.                                                       */
+/* Readings: everything in binary32 with RNE; alpha = 0.5 takes both powers  */
+/* as square roots (correctly rounded, so bit-exact); other alphas use powf; */
+/* the smoothed weight is the binary32 product w * s; the smoothed          */
+/* activation is the binary32 quotient x / s; the integer product is exact   */
+/* (int64 here); y = fp16((float(acc) * sx[m]) * sw[n]), evaluated left to   */
+/* right.  Pinned by the SmoothQuant identity, the alpha = 0.5 balance and   */
+/* the alpha = 0 / 1 limits, brute force of the row quantizers, numpy's      */
+/* int64 matmul and an error bound of the whole product.                     */
+/* ------------------------------------------------------------------------ */
+void orc_col_absmax_f16(const uint16_t *x, int64_t rows, int64_t cols, float *out)
+{
+    for (int64_t j = 0; j < cols; j++)
+        out[j] = 0.0f;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t j = 0; j < cols; j++) {
+            const float a = fabsf(orc_f16_to_f32(x[r * cols + j]));
+            if (a > out[j]) out[j] = a;
+        }
+}
+
+void orc_col_absmax_f32(const float *w, int64_t rows, int64_t cols, float *out)
+{
+    for (int64_t j = 0; j < cols; j++)
+        out[j] = 0.0f;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t j = 0; j < cols; j++) {
+            const float a = fabsf(w[r * cols + j]);
+            if (a > out[j]) out[j] = a;
+        }
+}
+
+void orc_smooth_factors(const float *act_max, const float *w_max, int64_t cols, float alpha, float *s)
+{
+    for (int64_t j = 0; j < cols; j++) {
+        const float w = w_max[j] < 1e-5f ? 1e-5f : w_max[j];
+        float num, den;
+        if (alpha == 0.5f) {
+            num = sqrtf(act_max[j]);
+            den = sqrtf(w);
+        } else {
+            num = powf(act_max[j], alpha);
+            den = powf(w, 1.0f - alpha);
+        }
+        float v = num / den;
+        s[j] = v < 1e-5f ? 1e-5f : v;
+    }
+}
+
+/* W [n_out][n_in] fp32, s [n_in] (NULL: no smoothing) -> q int8 [n_out][n_in],
+ * sw [n_out]: row n of W * diag(s) quantized symmetrically to INT8. */
+int orc_w8a8_quant_weight(const float *w, const float *s, int64_t n_out, int64_t n_in,
+                          int8_t *q, float *sw)
+{
+    int failed = 0;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_out; n++) {
+        float *v = (float *)malloc((size_t)n_in * sizeof(float));
+        int32_t *c = (int32_t *)malloc((size_t)n_in * sizeof(int32_t));
+        if (!v || !c) {
+            #pragma omp atomic write
+            failed = 1;
+            free(v);
+            free(c);
+            continue;
+        }
+        for (int64_t k = 0; k < n_in; k++)
+            v[k] = s ? w[n * n_in + k] * s[k] : w[n * n_in + k];
+        float sc;
+        int32_t z;
+        orc_quantize_group(v, n_in, 8, 1, &sc, &z, c);
+        for (int64_t k = 0; k < n_in; k++)
+            q[n * n_in + k] = (int8_t)c[k];
+        sw[n] = sc;
+        free(v);
+        free(c);
+    }
+    return failed ? 2 : 0;
+}
+
+/* x fp16 [m][k], s [k] (NULL: no smoothing) -> q int8 [m][k], sx [m]: token
+ * row m of x * diag(s)^-1 quantized symmetrically to INT8. */
+int orc_w8a8_quant_act(const uint16_t *x, const float *s, int64_t m, int64_t k, int8_t *q, float *sx)
+{
+    int failed = 0;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; r++) {
+        float *v = (float *)malloc((size_t)k * sizeof(float));
+        int32_t *c = (int32_t *)malloc((size_t)k * sizeof(int32_t));
+        if (!v || !c) {
+            #pragma omp atomic write
+            failed = 1;
+            free(v);
+            free(c);
+            continue;
+        }
+        for (int64_t j = 0; j < k; j++) {
+            const float xv = orc_f16_to_f32(x[r * k + j]);
+            v[j] = s ? xv / s[j] : xv;
+        }
+        float sc;
+        int32_t z;
+        orc_quantize_group(v, k, 8, 1, &sc, &z, c);
+        for (int64_t j = 0; j < k; j++)
+            q[r * k + j] = (int8_t)c[j];
+        sx[r] = sc;
+        free(v);
+        free(c);
+    }
+    return failed ? 2 : 0;
+}
+
+/* acc[m][n] = sum_k qx[m][k] qw[n][k] exactly; y = fp16((float(acc) sx[m]) sw[n]). */
+void orc_w8a8_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+                   int64_t m, int64_t n_out, int64_t k, int64_t *acc, uint16_t *y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_out; n++)
+        for (int64_t i = 0; i < m; i++) {
+            int64_t a = 0;
+            for (int64_t j = 0; j < k; j++)
+                a += (int64_t)qx[i * k + j] * (int64_t)qw[n * k + j];
+            if (acc)
+                acc[i * n_out + n] = a;
+            const float v = ((float)a * sx[i]) * sw[n];
+            y[i * n_out + n] = orc_f32_to_f16(v);
+        }
 }

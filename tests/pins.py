@@ -568,6 +568,102 @@ def pin_kv_cache_sizes(orc, quick=False):
     assert q.nbytes * 2 == x.nbytes
 
 
+# ---------------------------------------------------------------------------
+# W8A8 with SmoothQuant (the interview guide's §4.2).
+# ---------------------------------------------------------------------------
+def _sq_case(seed, m=24, n=40, k=96):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, rng.choice(k, 3, replace=False)] *= 60.0           # activation outlier channels
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    return x.astype(np.float16), w
+
+
+def pin_sq_balance_and_limits(orc, quick=False):
+    """alpha = 0.5 balances the channel maxima of X diag(s)^-1 and diag(s) W;
+    alpha = 1 moves everything to the weights (activation maxima 1), alpha = 0
+    leaves it in the activations (weight maxima 1).  Channel maxima by numpy."""
+    x, w = _sq_case(81)
+    a = np.abs(x.astype(np.float32)).max(axis=0)
+    wm = np.abs(w).max(axis=0)
+    assert np.array_equal(orc.col_absmax_f16(x.view(np.uint16)), a)
+    assert np.array_equal(orc.col_absmax_f32(w), wm)
+    s = orc.smooth_factors(a, wm, 0.5).astype(np.float64)
+    np.testing.assert_allclose(a / s, wm * s, rtol=4e-7)
+    s1 = orc.smooth_factors(a, wm, 1.0).astype(np.float64)
+    np.testing.assert_allclose(a / s1, 1.0, rtol=4e-7)
+    s0 = orc.smooth_factors(a, wm, 0.0).astype(np.float64)
+    np.testing.assert_allclose(wm * s0, 1.0, rtol=4e-7)
+    s3 = orc.smooth_factors(a, wm, 0.75).astype(np.float64)
+    np.testing.assert_allclose(s3, a ** 0.75 / wm ** 0.25, rtol=2e-6)
+
+
+def pin_sq_clamps(orc, quick=False):
+    a = np.array([4.0, 0.0, 9.0, 0.0], dtype=np.float32)
+    wm = np.array([0.0, 0.25, 1e-7, 0.0], dtype=np.float32)
+    s = orc.smooth_factors(a, wm, 0.5).astype(np.float64)
+    # weight maxima floored at 1e-5 before the power; s floored at 1e-5
+    np.testing.assert_allclose(s, [2.0 / np.sqrt(1e-5), 1e-5, 3.0 / np.sqrt(1e-5), 1e-5], rtol=2e-7)
+
+
+def pin_w8a8_row_quantizers(orc, quick=False):
+    """Both INT8 row quantizers pass the brute-force check; with smoothing they
+    equal the unsmoothed quantizer on numpy's binary32 w * s and x / s."""
+    x, w = _sq_case(82)
+    qw, sw = orc.w8a8_quant_weight(w)
+    _check_rows(w, qw, sw, 8, "weights")
+    qx, sx = orc.w8a8_quant_act(x.view(np.uint16))
+    _check_rows(x.astype(np.float32), qx, sx, 8, "activations")
+    s = orc.smooth_factors(orc.col_absmax_f16(x.view(np.uint16)), orc.col_absmax_f32(w), 0.5)
+    qws, sws = orc.w8a8_quant_weight(w, s)
+    q2, s2 = orc.w8a8_quant_weight(w * s[None, :])
+    assert np.array_equal(qws, q2) and np.array_equal(sws.view(np.uint32), s2.view(np.uint32))
+    qxs, sxs = orc.w8a8_quant_act(x.view(np.uint16), s)
+    xs = x.astype(np.float32) / s[None, :]
+    for r in range(xs.shape[0]):
+        sc, z, q = orc.quantize_group(xs[r], bits=8, symmetric=True)
+        assert z == 0 and np.float32(sc) == sxs[r] and np.array_equal(q, qxs[r].astype(np.int32)), f"row {r}"
+
+
+def pin_w8a8_gemm(orc, quick=False):
+    rng = np.random.default_rng(83)
+    qx = rng.integers(-128, 128, size=(17, 300)).astype(np.int8)
+    qw = rng.integers(-128, 128, size=(23, 300)).astype(np.int8)
+    ones_x, ones_w = np.ones(17, np.float32), np.ones(23, np.float32)
+    y, acc = orc.w8a8_gemm(qx, ones_x, qw, ones_w)
+    assert np.array_equal(acc, qx.astype(np.int64) @ qw.astype(np.int64).T)
+    # small integer sums are exact in fp16; power-of-two scales scale exactly
+    qs = (rng.integers(-3, 4, size=(5, 64))).astype(np.int8)
+    ws = (rng.integers(-3, 4, size=(6, 64))).astype(np.int8)
+    y, acc = orc.w8a8_gemm(qs, np.full(5, 0.25, np.float32), ws, np.full(6, 8.0, np.float32))
+    assert np.array_equal(y.view(np.float16).astype(np.float64), (qs.astype(np.int64) @ ws.astype(np.int64).T) * 2.0)
+
+
+def pin_w8a8_error_bound(orc, quick=False):
+    """The smoothed W8A8 product against the binary64 X W^T: per element,
+    |y - xw| <= sum_k (|x^_k| sw / 2 + |w^_k| sx / 2 + sx sw / 4) + fp16 rounding."""
+    for seed in (84, 85):
+        x, w = _sq_case(seed, m=32, n=48, k=256)
+        s = orc.smooth_factors(orc.col_absmax_f16(x.view(np.uint16)), orc.col_absmax_f32(w), 0.5)
+        qw, sw = orc.w8a8_quant_weight(w, s)
+        qx, sx = orc.w8a8_quant_act(x.view(np.uint16), s)
+        y, _ = orc.w8a8_gemm(qx, sx, qw, sw)
+        yf = y.view(np.float16).astype(np.float64)
+        xd, wd, sd = x.astype(np.float64), w.astype(np.float64), s.astype(np.float64)
+        ref = xd @ wd.T
+        xh, wh = np.abs(xd / sd), np.abs(wd * sd)
+        sxd, swd = sx.astype(np.float64)[:, None], sw.astype(np.float64)[None, :]
+        bound = (xh @ np.ones((xh.shape[1], 1))) * swd / 2 + sxd * (wh.sum(axis=1))[None, :] / 2
+        bound += sxd * swd * x.shape[1] / 4 + np.abs(yf) * 2.0 ** -10 + 1e-6 * (np.abs(xd) @ np.abs(wd).T)
+        assert (np.abs(yf - ref) <= bound).all(), f"seed {seed}: {np.abs(yf - ref).max()} vs bound"
+        # and smoothing helps: the same product without smoothing has a larger worst error here
+        qw0, sw0 = orc.w8a8_quant_weight(w)
+        qx0, sx0 = orc.w8a8_quant_act(x.view(np.uint16))
+        y0, _ = orc.w8a8_gemm(qx0, sx0, qw0, sw0)
+        err0 = np.abs(y0.view(np.float16).astype(np.float64) - ref).max()
+        assert np.abs(yf - ref).max() < err0, "smoothing should reduce the error on outlier activations"
+
+
 ALL_PINS = [
     pin_worked_example, pin_brute_force, pin_ties_to_even, pin_zero_clip,
     pin_reconstruction_bound, pin_idempotence, pin_grid_exact, pin_constant_groups,
@@ -576,4 +672,5 @@ ALL_PINS = [
     pin_dequant_int8, pin_reconstruction_bound_int8,
     pin_kv_brute_force, pin_kv_worked_example, pin_kv_transpose, pin_kv_bound, pin_kv_ties_and_zero,
     pin_kv_cache_sizes,
+    pin_sq_balance_and_limits, pin_sq_clamps, pin_w8a8_row_quantizers, pin_w8a8_gemm, pin_w8a8_error_bound,
 ]

@@ -55,6 +55,19 @@ MUTANTS = {
     "kv_dequant_double_f16": ("out[r * d + i] = orc_f32_to_f16((float)q[r * d + i] * scale[r]);",
                               "out[r * d + i] = orc_f32_to_f16((float)q[r * d + i] * orc_f16_to_f32(orc_f32_to_f16(scale[r])));"),
     "kv_cache_bytes_one_side": ("return 2.0 * (double)layers", "return 1.0 * (double)layers"),
+    "sq_ratio_inverted": ("float v = num / den;", "float v = den / num;"),
+    "sq_pow_exponents_swapped": ("num = powf(act_max[j], alpha);\n            den = powf(w, 1.0f - alpha);",
+                                 "num = powf(act_max[j], 1.0f - alpha);\n            den = powf(w, alpha);"),
+    "sq_no_weight_floor": ("const float w = w_max[j] < 1e-5f ? 1e-5f : w_max[j];", "const float w = w_max[j];"),
+    "sq_colmax_no_abs": ("const float a = fabsf(orc_f16_to_f32(x[r * cols + j]));",
+                         "const float a = orc_f16_to_f32(x[r * cols + j]);"),
+    "w8a8_act_multiplied": ("v[j] = s ? xv / s[j] : xv;", "v[j] = s ? xv * s[j] : xv;"),
+    "w8a8_weight_divided": ("v[k] = s ? w[n * n_in + k] * s[k] : w[n * n_in + k];",
+                            "v[k] = s ? w[n * n_in + k] / s[k] : w[n * n_in + k];"),
+    "w8a8_epilogue_scale_swap": ("const float v = ((float)a * sx[i]) * sw[n];",
+                                 "const float v = ((float)a * sw[n]) * sw[n];"),
+    "w8a8_gemm_k_shift": ("a += (int64_t)qx[i * k + j] * (int64_t)qw[n * k + j];",
+                          "a += (int64_t)qx[i * k + j] * (int64_t)qw[n * k + (j + 1) % k];"),
 }
 
 
