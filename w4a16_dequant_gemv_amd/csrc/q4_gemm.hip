@@ -33,7 +33,7 @@
 // step, done afterwards without pipelining.
 //
 // LDS rows are 128 bytes (64 halves); the eight 16-byte chunks of row r are
-// stored at chunk ^ swz(r) (see below) so that fragment reads (16 rows, one
+// stored at chunk ^ swz(r) (gemm_tile.h) so that fragment reads (16 rows, one
 // chunk each), x stores (whole rows) and weight stores (8 rows, two half-rows
 // of 4 chunks each) all hit distinct 16-byte bank groups, whether the lanes
 // are served 8 at a time over 32 banks or 16 at a time over 64 banks.
@@ -46,20 +46,11 @@
 // the packed weights (BN rows x n_in/2 bytes each), which its L2 shares.
 #include <type_traits>
 
+#include "gemm_tile.h"
 #include "q4_device.h"
 #include "q4_launch.h"
 
 namespace {
-
-constexpr int kXcds = 8;
-constexpr int kStages = 3;
-constexpr int kGroupM = 2;
-// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
-constexpr int kBufferFlags = 0x00020000;
-
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100,
-              kSgDsWrite = 0x200;
 
 // Eight codes of one packed word -> eight fp16 weights s * (c - z) in
 // natural order (c0, c1), (c2, c3), ...: the codes are split into even and
@@ -94,18 +85,6 @@ __device__ __forceinline__ u32x2 dequant_byte_word(uint32_t w, f16x2 bias, f16x2
     return r;
 }
 
-// Chunk permutation of LDS row r, a function of r & 15.  Its low two bits
-// differ across any 4 consecutive rows and across the 4 even (or 4 odd) rows
-// of an aligned group of 8; the whole value differs across any aligned group
-// of 8 rows and across the 8 even (or 8 odd) rows of an aligned group of 16.
-__device__ __forceinline__ int swz(int r)
-{
-    return ((r ^ (r >> 2)) & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
-}
-
-// Scheduling pattern of one substep: each of its N MFMAs is followed by one
-// LDS read (the first NDSR slots), NVALU vector ALU instructions, one LDS
-// write (the last NDSW slots) and one global load (the first NVMEM slots).
 template <int I, int N, int NDSR, int NDSW, int NVMEM, int NVALU>
 __device__ __forceinline__ void interleave()
 {
@@ -152,18 +131,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     extern __shared__ __attribute__((aligned(16))) char smem[];   // [kStages][A | B]
 
     // --- tile selection (XCD-aware) ---
-    const int tiles = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int xcd = bid % kXcds, local = bid / kXcds;
-    const int per_xcd = tiles / kXcds, extra = tiles % kXcds;
-    // XCDs 0..extra-1 own per_xcd + 1 consecutive tiles, the rest per_xcd
-    const int t = xcd < extra ? xcd * (per_xcd + 1) + local
-                              : extra * (per_xcd + 1) + (xcd - extra) * per_xcd + local;
-    const int band = t / (kGroupM * tiles_n);
-    const int band_m = min(kGroupM, tiles_m - band * kGroupM);
-    const int in_band = t - band * kGroupM * tiles_n;
-    const int tile_n = in_band / band_m;
-    const int tile_m = band * kGroupM + in_band % band_m;
+    int tile_m, tile_n;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
     const int tid = threadIdx.x;
