@@ -19,6 +19,8 @@ Also measured in the same run and reported as extra keys:
   w8a16    -- INT8 decode (8 fused 7B layers, per-channel) and prefill (g=128),
   kv_codec -- the KV-cache codec on one 70B-shaped layer cache (GB/s) and the
               decode-time flush of 256 window blocks into a block pool,
+  w8a8_smoothquant -- the int8 product at m=2048 on the 7B shapes (TOP/s) and
+              the whole smoothed layer (activation quantization + product),
   cpu_baseline -- the CPU oracle (dequantize + binary64 product) timed on
                   this host's cores on a bounded sample of the decode step.
 
@@ -37,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -407,6 +410,45 @@ def bench_kv(args, dev):
     return res
 
 
+def bench_w8a8(args, dev):
+    """W8A8 with SmoothQuant at prefill (m = 2048) on the 7B projection shapes:
+    the int8 product alone (TOP/s against the 5.0 POP/s dense int8 peak) and
+    the whole layer per call (per-token activation quantization of x / s, then
+    the product)."""
+    import torch
+    from w4a16_dequant_gemv_amd import synthetic as syn, w8a8
+    out, tot_op, tot_t, tot_layer_t = [], 0, 0.0, 0.0
+    for i, lin in enumerate(syn.PREFILL_LINEARS):
+        w = syn.normal_weight_device(lin.n_out, lin.n_in, 4000 + i, 0.02, syn.n_outliers(lin.n_in), dev)
+        calib = syn.activations_f16_device(512, lin.n_in, 4200 + i, dev)
+        act_max = torch.zeros(lin.n_in, dtype=torch.float32, device=dev)
+        w8a8.absmax_update(calib, act_max)
+        layer = w8a8.W8A8Linear.from_float(w, act_max)
+        del w, calib
+        x = syn.activations_f16_device(syn.PREFILL_M, lin.n_in, 4100 + i, dev)
+        qx, sx = w8a8.quantize_act(x, layer.s)
+        y = torch.empty((syn.PREFILL_M, lin.n_out), dtype=torch.float16, device=dev)
+        reps = 20
+        g = capture(lambda: [w8a8.gemm(qx, sx, layer.qw, layer.sw, y) for _ in range(reps)])
+        el, _ = time_graph(g, 5, 3)
+        t = el / (5 * reps)
+        gl = capture(lambda: [(w8a8.quantize_act(x, layer.s, qx, sx), w8a8.gemm(qx, sx, layer.qw, layer.sw, y))
+                              for _ in range(reps)])
+        el, _ = time_graph(gl, 5, 3)
+        tl = el / (5 * reps)
+        op = 2 * syn.PREFILL_M * lin.n_out * lin.n_in
+        out.append(dict(shape=f"{syn.PREFILL_M}x{lin.n_out}x{lin.n_in}", gemm_us=round(t * 1e6, 2),
+                        tops=round(op / t / 1e12, 1), layer_us=round(tl * 1e6, 2)))
+        tot_op += op
+        tot_t += t
+        tot_layer_t += tl
+        del layer, x, qx, y, g, gl
+    torch.cuda.empty_cache()
+    tops = round(tot_op / tot_t / 1e12, 1)
+    return dict(shapes=out, tops=tops, frac_int8_peak=round(tops / INT8_PEAK_TOPS, 4),
+                layer_tops=round(tot_op / tot_layer_t / 1e12, 1))
+
+
 def bench_stress_and_quantize(args, dev):
     import torch
     import w4a16_dequant_gemv_amd as w4
@@ -510,6 +552,8 @@ def main():
         log(f"int8 (W8A16): {extras['int8']}")
         extras["kv"] = bench_kv(args, dev)
         log(f"kv codec: {extras['kv']}")
+        extras["w8a8"] = bench_w8a8(args, dev)
+        log(f"w8a8: {extras['w8a8']}")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host_w, args.cpu_seconds)
@@ -554,6 +598,7 @@ def main():
         record["single_gemv_4096x4096"] = extras["single"]
         record["w8a16"] = extras["int8"]
         record["kv_codec"] = extras["kv"]
+        record["w8a8_smoothquant"] = extras["w8a8"]
     print(json.dumps(record), flush=True)
 
 

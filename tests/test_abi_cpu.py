@@ -14,7 +14,7 @@ from w4a16_dequant_gemv_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
-HEADERS = [HEADER, os.path.join(ROOT, "include", "kv_codec.h")]
+HEADERS = [HEADER, os.path.join(ROOT, "include", "kv_codec.h"), os.path.join(ROOT, "include", "w8a8.h")]
 
 P16 = 0x10000      # 16-byte aligned placeholder address (never dereferenced)
 P2 = 0x10002       # 2-byte but not 16-byte aligned
@@ -24,7 +24,7 @@ def header_functions():
     names = set()
     for h in HEADERS:
         text = open(h, encoding="utf-8").read()
-        names |= set(re.findall(r"^\s*(?:int|const char \*)\s*((?:q[48]|kv)_\w+)\s*\(", text, re.M))
+        names |= set(re.findall(r"^\s*(?:int|const char \*)\s*((?:q[48]|kv|sq|w8a8)_\w+)\s*\(", text, re.M))
     return sorted(names)
 
 
@@ -232,3 +232,28 @@ def test_kv_flush_rejects(L):
     assert call(bits=5) == _lib.Q4_ERR_SHAPE
     assert call(dst=P16 + 2) == _lib.Q4_ERR_ALIGN
     assert call(vp=P16 + 4) == _lib.Q4_ERR_ALIGN
+
+
+def test_w8a8_rejects(L):
+    # calibration maxima
+    assert L.sq_absmax_update_f16(None, 4, 64, P16, None) == _lib.Q4_ERR_NULL
+    assert L.sq_absmax_update_f16(P16, 4, 60, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.sq_absmax_update_f32(P16, 0, 64, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.sq_absmax_update_f32(P16 + 4, 4, 64, P16, None) == _lib.Q4_ERR_ALIGN
+    # factors
+    assert L.sq_smooth_factors(P16, P16, 64, 1.5, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.sq_smooth_factors(P16, P16, 64, float("nan"), P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.sq_smooth_factors(P16, None, 64, 0.5, P16, None) == _lib.Q4_ERR_NULL
+    # quantizers: k a multiple of 32 in [32, 32768]
+    assert L.w8a8_quantize_weight(P16, None, 8, 100, P16, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.w8a8_quantize_weight(P16, None, 8, 32800, P16, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.w8a8_quantize_weight(P16, P16 + 4, 8, 96, P16, P16, None) == _lib.Q4_ERR_ALIGN
+    assert L.w8a8_quantize_act(P16, None, 0, 96, P16, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.w8a8_quantize_act(P16 + 2, None, 4, 96, P16, P16, None) == _lib.Q4_ERR_ALIGN
+    assert L.w8a8_quantize_act(P16, None, 4, 96, None, P16, None) == _lib.Q4_ERR_NULL
+    # product
+    assert L.w8a8_gemm(P16, P16, P16, P16, 4, 8, 48, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.w8a8_gemm(P16, P16, P16, P16, 4, 0, 64, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.w8a8_gemm(P16 + 8, P16, P16, P16, 4, 8, 64, P16, None) == _lib.Q4_ERR_ALIGN
+    assert L.w8a8_gemm(P16, P16, P16, P16, 4, 8, 64, P16 + 1, None) == _lib.Q4_ERR_ALIGN
+    assert L.w8a8_gemm(P16, None, P16, P16, 4, 8, 64, P16, None) == _lib.Q4_ERR_NULL

@@ -30,6 +30,12 @@ SIGNATURES = {
     "kv_dequant_tokens": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),
     "kv_dequant_channels": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _p, _p]),
     "kv_flush_blocks": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _p, _p, _p, _p]),
+    "sq_absmax_update_f16": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
+    "sq_absmax_update_f32": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
+    "sq_smooth_factors": (ctypes.c_int, [_p, _p, _i32, ctypes.c_float, _p, _p]),
+    "w8a8_quantize_weight": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p]),
+    "w8a8_quantize_act": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p]),
+    "w8a8_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p]),
 }
 
 

@@ -3,7 +3,7 @@
     python -m w4a16_dequant_gemv_amd.build
 
 Every translation unit is compiled with packed-fp32 instruction selection
-disabled; the weight quantizer's and the KV codec's units additionally keep
+disabled; the weight quantizer's, the KV codec's and the W8A8 units additionally keep
 each fp32 operation separate (no FMA contraction) and use correctly rounded
 fp32 division, which their bit-exactness depends on.
 """
@@ -29,8 +29,9 @@ EXACT_FP32 = ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "
 PER_FILE = {
     "q4_quantize.hip": EXACT_FP32,
     "kv_codec.hip": EXACT_FP32,
+    "w8a8.hip": EXACT_FP32,
 }
-SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip", "kv_codec.hip"]
+SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip", "kv_codec.hip", "w8a8.hip"]
 
 
 def _compile(src):

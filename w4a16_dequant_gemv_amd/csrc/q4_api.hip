@@ -2,6 +2,7 @@
 // (before any HIP call), then one launch on the caller's stream.
 #include "w4a16.h"
 #include "kv_codec.h"
+#include "w8a8.h"
 
 #include "q4_launch.h"
 
@@ -57,6 +58,11 @@ int check_linear(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
         return Q4_ERR_ALIGN;
     return Q4_OK;
 }
+
+// W8A8 shapes: k a multiple of 32 in [32, 32768]; rows and outputs in [1, 2^24].
+int check_w8a8_k(int64_t k) { return (k >= 32 && k <= 32768 && k % 32 == 0) ? Q4_OK : Q4_ERR_SHAPE; }
+
+int check_rows(int64_t r) { return (r >= 1 && r <= kMaxRows) ? Q4_OK : Q4_ERR_SHAPE; }
 
 // KV codec shapes: head dimension d a multiple of 8 in [8, 512]; per-channel
 // blocks of t tokens fit 32 rows per thread (t <= 32 * (2048 / d)).
@@ -251,6 +257,62 @@ int kv_flush_blocks(const uint16_t *k, const uint16_t *v, int64_t blocks, int32_
         return Q4_ERR_ALIGN;
     return finish(kv_launch_flush(k, v, blocks, t, d, bits, dst, pool_blocks, k_pool, k_scale, v_pool,
                                   v_scale, (hipStream_t)stream));
+}
+
+int sq_absmax_update_f16(const uint16_t *x, int64_t rows, int32_t cols, float *amax, void *stream)
+{
+    if (!x || !amax) return Q4_ERR_NULL;
+    if (check_rows(rows) || cols < 8 || cols > kMaxIn || cols % 8 != 0 || rows * cols > kMaxElems)
+        return Q4_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(amax, 4)) return Q4_ERR_ALIGN;
+    return finish(w8a8_launch_col_absmax(x, false, rows, cols, amax, (hipStream_t)stream));
+}
+
+int sq_absmax_update_f32(const float *w, int64_t rows, int32_t cols, float *amax, void *stream)
+{
+    if (!w || !amax) return Q4_ERR_NULL;
+    if (check_rows(rows) || cols < 8 || cols > kMaxIn || cols % 8 != 0 || rows * cols > kMaxElems)
+        return Q4_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(amax, 4)) return Q4_ERR_ALIGN;
+    return finish(w8a8_launch_col_absmax(w, true, rows, cols, amax, (hipStream_t)stream));
+}
+
+int sq_smooth_factors(const float *act_max, const float *w_max, int32_t n, float alpha, float *s,
+                      void *stream)
+{
+    if (!act_max || !w_max || !s) return Q4_ERR_NULL;
+    if (n <= 0 || n > kMaxIn || !(alpha >= 0.0f && alpha <= 1.0f)) return Q4_ERR_SHAPE;
+    if (!aligned(act_max, 4) || !aligned(w_max, 4) || !aligned(s, 4)) return Q4_ERR_ALIGN;
+    return finish(w8a8_launch_smooth_factors(act_max, w_max, n, alpha, s, (hipStream_t)stream));
+}
+
+int w8a8_quantize_weight(const float *w, const float *s, int64_t n_out, int64_t k, int8_t *qw,
+                         float *sw, void *stream)
+{
+    if (!w || !qw || !sw) return Q4_ERR_NULL;
+    if (check_rows(n_out) || check_w8a8_k(k) || n_out * k > kMaxElems) return Q4_ERR_SHAPE;
+    if (!aligned(w, 16) || (s && !aligned(s, 16)) || !aligned(qw, 16) || !aligned(sw, 4)) return Q4_ERR_ALIGN;
+    return finish(w8a8_launch_quant_weight(w, s, n_out, (int)k, qw, sw, (hipStream_t)stream));
+}
+
+int w8a8_quantize_act(const uint16_t *x, const float *s, int64_t m, int64_t k, int8_t *qx,
+                      float *sx, void *stream)
+{
+    if (!x || !qx || !sx) return Q4_ERR_NULL;
+    if (check_rows(m) || check_w8a8_k(k) || m * k > kMaxElems) return Q4_ERR_SHAPE;
+    if (!aligned(x, 16) || (s && !aligned(s, 16)) || !aligned(qx, 16) || !aligned(sx, 4)) return Q4_ERR_ALIGN;
+    return finish(w8a8_launch_quant_act(x, s, m, (int)k, qx, sx, (hipStream_t)stream));
+}
+
+int w8a8_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw, int64_t m,
+              int64_t n_out, int64_t k, uint16_t *y, void *stream)
+{
+    if (!qx || !sx || !qw || !sw || !y) return Q4_ERR_NULL;
+    if (check_rows(m) || check_rows(n_out) || check_w8a8_k(k)) return Q4_ERR_SHAPE;
+    if (m * k > kMaxElems || n_out * k > kMaxElems || m * n_out > kMaxElems) return Q4_ERR_SHAPE;
+    if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 2))
+        return Q4_ERR_ALIGN;
+    return finish(w8a8_launch_gemm(qx, sx, qw, sw, m, n_out, k, y, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -34,3 +34,15 @@ hipError_t kv_launch_dequant_tokens(const int8_t *q, const float *scale, int64_t
                                     hipStream_t stream);
 hipError_t kv_launch_dequant_channels(const int8_t *q, const float *scale, int64_t blocks, int t, int d,
                                       uint16_t *out, hipStream_t stream);
+
+// W8A8 with SmoothQuant (w8a8.hip); cols % 8 == 0, k % 32 == 0, k <= 32768.
+hipError_t w8a8_launch_col_absmax(const void *src, bool f32, int64_t rows, int cols, float *out,
+                                  hipStream_t stream);
+hipError_t w8a8_launch_smooth_factors(const float *act_max, const float *w_max, int n, float alpha, float *s,
+                                      hipStream_t stream);
+hipError_t w8a8_launch_quant_weight(const float *w, const float *s, int64_t n_out, int n_in, int8_t *q, float *sw,
+                                    hipStream_t stream);
+hipError_t w8a8_launch_quant_act(const uint16_t *x, const float *s, int64_t m, int k, int8_t *q, float *sx,
+                                 hipStream_t stream);
+hipError_t w8a8_launch_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw, int64_t m,
+                            int64_t n_out, int64_t k, uint16_t *y, hipStream_t stream);

@@ -1,0 +1,569 @@
+// w8a8.hip -- W8A8 linear layer with SmoothQuant on the gfx950 int8 matrix
+// cores: calibration maxima, smoothing factors, per-channel INT8 weights,
+// per-token INT8 activations and the int8 x int8 -> int32 product.
+//
+// [Guide] §4.2 (SmoothQuant): activations are hard to quantize because of
+// outlier channels, weights are easy, so Y = (X diag(s)^-1)(diag(s) W) moves
+// difficulty from X to W with s_j = max|X_j|^alpha / max|W_j|^(1 - alpha)
+// (alpha = 0.5 in practice; max|W_j| taken over every linear sharing the
+// input; both clamped at 1e-5), and diag(s)^-1 can be folded into the
+// preceding LayerNorm.  W8A8 runs the product on INT8 matrix units at twice
+// the fp16 rate ([Guide] §4.2, §2.3); INT8 weights carry one scale per
+// output channel ([Guide] §2.2); activations are quantized per token at run
+// time with the symmetric map of [Guide] §6's per-token listing.
+//
+// Arithmetic (this unit is built without FMA contraction and with correctly
+// rounded division and square root): the smoothed weight is w * s and the
+// smoothed activation x / s in binary32; scale = max|.| / 127 floored at
+// 1e-8; code = clamp(round(v / scale), -128, 127), where the product with the
+// hardware reciprocal decides unless it lies within 2^-14 of a half-integer
+// (then the correctly rounded division does), so codes are bit-exact; the
+// integer product is exact in int32 (|code| <= 128, K <= 32768); and
+// y = fp16((float(acc) * sx[m]) * sw[n]).  Every output is therefore
+// bit-exact; only alpha != 0.5 (powf) may differ from another libm by an ulp.
+//
+// GEMM tiling follows the W4A16 kernel (q4_gemm.hip) without the
+// dequantization: 256 x 128 output tiles, 4 waves stacked along m (64 x 128
+// each), k in steps of 128 bytes = four v_mfma_i32_32x32x32_i8 substeps,
+// three LDS stages of (x tile | weight tile) with one barrier per step, three
+// register sets of global loads issued three steps ahead, the XCD-aware tile
+// order and the conflict-free chunk swizzle of gemm_tile.h.  The MFMAs take
+// the weight fragment first, so each lane holds runs of 4 consecutive output
+// channels and the epilogue stores whole rows through LDS.
+#include <type_traits>
+
+#include "gemm_tile.h"
+#include "q4_device.h"
+#include "q4_launch.h"
+
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr float kQmax = 127.0f;
+
+// ---------------------------------------------------------------------------
+// Calibration: column maxima of |x| folded into out[] with an atomic maximum
+// on the float bits (non-negative floats order like their bit patterns), so
+// several batches (or several linears sharing an input) accumulate exactly.
+// ---------------------------------------------------------------------------
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void col_absmax_kernel(const void *__restrict__ src, int64_t rows, int cols,
+                                                              int rows_per_block, float *__restrict__ out)
+{
+    const int cpr = cols / 8;
+    const int c = blockIdx.x * kThreads + threadIdx.x;
+    if (c >= cpr) return;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = r0 + rows_per_block < rows ? r0 + rows_per_block : rows;
+    float mx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx[e] = 0.0f;
+#pragma unroll 4
+    for (int64_t r = r0; r < r1; ++r) {
+        float v[8];
+        if constexpr (F32) {
+            const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(src) + r * cols + c * 8);
+            const f32x4 a = p[0], b = p[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = a[e];
+                v[e + 4] = b[e];
+            }
+        } else {
+            const u32x4 raw =
+                *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(src) + r * cols + c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = half_bits_to_float((uint16_t)(raw[e >> 1] >> (16 * (e & 1))));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(v[e]));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        atomicMax(reinterpret_cast<unsigned int *>(out) + c * 8 + e, __float_as_uint(mx[e]));
+}
+
+__global__ __launch_bounds__(kThreads) void smooth_factors_kernel(const float *__restrict__ act_max,
+                                                                  const float *__restrict__ w_max, int n,
+                                                                  float alpha, float *__restrict__ s)
+{
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const float w = w_max[i] < 1e-5f ? 1e-5f : w_max[i];
+    float num, den;
+    if (alpha == 0.5f) {
+        num = __builtin_sqrtf(act_max[i]);
+        den = __builtin_sqrtf(w);
+    } else {
+        num = powf(act_max[i], alpha);
+        den = powf(w, 1.0f - alpha);
+    }
+    const float v = num / den;
+    s[i] = v < 1e-5f ? 1e-5f : v;
+}
+
+// ---------------------------------------------------------------------------
+// Row quantizers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sym_scale(float amax)
+{
+    const float s = amax / kQmax;
+    return s < 1e-8f ? 1e-8f : s;
+}
+
+// round(v / s) clamped to int8 (see the file comment for the reciprocal test)
+__device__ __forceinline__ uint32_t sym_code(float v, float s, float r)
+{
+    const float a = v * r;
+    float c = __builtin_rintf(a);
+    if (fabsf(a - c) > 0.5f - 0x1p-14f || fabsf(a) >= 128.0f) c = __builtin_rintf(v / s);
+    c = fminf(fmaxf(c, -kQmax - 1.0f), kQmax);
+    return (uint32_t)(int32_t)c & 0xFFu;
+}
+
+__device__ __forceinline__ u32x2 sym_codes8(const float v[8], float s, float r)
+{
+    u32x2 w = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= sym_code(v[e], s, r) << (8 * (e & 3));
+    return w;
+}
+
+// Maximum over the workgroup (every thread gets it).
+__device__ __forceinline__ float block_max(float a, float *red)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    return a;
+}
+
+// One workgroup per weight row: w * s, its maximum, then the codes (the row
+// is read twice; the second read is served by the caches).
+__global__ __launch_bounds__(kThreads) void quant_weight_kernel(const float *__restrict__ w,
+                                                                const float *__restrict__ s, int n_in,
+                                                                int8_t *__restrict__ q, float *__restrict__ sw)
+{
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float *wr = w + row * n_in;
+    const int cpr = n_in / 8;
+    auto load8 = [&](int c, float v[8]) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(wr + c * 8);
+        const f32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = a[e];
+            v[e + 4] = b[e];
+        }
+        if (s) {
+            const f32x4 *sp = reinterpret_cast<const f32x4 *>(s + c * 8);
+            const f32x4 sa = sp[0], sb = sp[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = v[e] * sa[e];
+                v[e + 4] = v[e + 4] * sb[e];
+            }
+        }
+    };
+    float a = 0.0f;
+    for (int c = threadIdx.x; c < cpr; c += kThreads) {
+        float v[8];
+        load8(c, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+    }
+    const float sc = sym_scale(block_max(a, red));
+    const float rc = __builtin_amdgcn_rcpf(sc);
+    for (int c = threadIdx.x; c < cpr; c += kThreads) {
+        float v[8];
+        load8(c, v);
+        *reinterpret_cast<u32x2 *>(q + row * n_in + c * 8) = sym_codes8(v, sc, rc);
+    }
+    if (threadIdx.x == 0) sw[row] = sc;
+}
+
+// One workgroup per token row, the row's x / s kept in registers (CPT chunks
+// of 8 per thread, k <= CPT * 2048).
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__restrict__ x,
+                                                             const float *__restrict__ s, int k,
+                                                             int8_t *__restrict__ q, float *__restrict__ sx)
+{
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const int cpr = k / 8;
+    float v[CPT][8];
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+        if (c < cpr) {
+            const u32x4 raw = *reinterpret_cast<const u32x4 *>(x + row * k + c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] = half_bits_to_float((uint16_t)(raw[e >> 1] >> (16 * (e & 1))));
+            if (s) {
+                const f32x4 *sp = reinterpret_cast<const f32x4 *>(s + c * 8);
+                const f32x4 sa = sp[0], sb = sp[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[i][e] = v[i][e] / sa[e];
+                    v[i][e + 4] = v[i][e + 4] / sb[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
+        }
+    }
+    const float sc = sym_scale(block_max(a, red));
+    const float rc = __builtin_amdgcn_rcpf(sc);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        if (c < cpr) *reinterpret_cast<u32x2 *>(q + row * k + c * 8) = sym_codes8(v[i], sc, rc);
+    }
+    if (threadIdx.x == 0) sx[row] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// int8 GEMM.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void w8a8_gemm_kernel(
+    const int8_t *__restrict__ qx, const float *__restrict__ sx, const int8_t *__restrict__ qw,
+    const float *__restrict__ sw, uint16_t *__restrict__ y, int m, int n_out, int k, int tiles_m, int tiles_n)
+{
+    constexpr int BK = 128, KSUB = 4;
+    constexpr int NW = WM * WN, THREADS = 64 * NW;
+    constexpr int WT_M = BM / WM, WT_N = BN / WN;
+    constexpr int TM = WT_M / 32, TN = WT_N / 32;
+    constexpr int A_CHUNKS = BM * 8 / THREADS, B_CHUNKS = BN * 8 / THREADS;
+    constexpr int A_PART = A_CHUNKS / KSUB, B_PART = B_CHUNKS / KSUB;
+    static_assert(A_PART * KSUB == A_CHUNKS && B_PART * KSUB == B_CHUNKS, "tiles do not split evenly");
+    static_assert(TM * 32 == WT_M && TN * 32 == WT_N, "wave tile not a multiple of 32");
+    static_assert(THREADS % 128 == 0, "row swizzles assume 16-row lane strides");
+    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
+    static_assert(kStages * STAGE <= 160 * 1024, "stages exceed LDS");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    int tile_m, tile_n;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave / WN, wave_n = wave % WN;
+    const int ksteps = k / BK, krem = k % BK;
+
+    // Per-tile buffer resources; rows past m or n_out read the last row (never stored).
+    const int rows_m = min(BM, m - m0), rows_n = min(BN, n_out - n0);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(qx + (int64_t)m0 * k), (short)0, rows_m * k, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t wr_ = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(qw + (int64_t)n0 * k), (short)0, rows_n * k, kBufferFlags);
+    uint32_t xoff[A_CHUNKS], woff[B_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+        const int c = tid + i * THREADS;                   // row c / 8, chunk c % 8
+        xoff[i] = (uint32_t)min(c >> 3, rows_m - 1) * (uint32_t)k + (uint32_t)(c & 7) * 16u;
+    }
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) {
+        const int c = tid + i * THREADS;
+        woff[i] = (uint32_t)min(c >> 3, rows_n - 1) * (uint32_t)k + (uint32_t)(c & 7) * 16u;
+    }
+    // LDS: chunk i of this lane sits THREADS / 8 rows (a multiple of 16) below chunk 0
+    const int st_row = tid >> 3;
+    const uint32_t a_st = st_row * 128 + (((tid & 7) ^ swz(st_row)) * 16);
+    const uint32_t b_st = A_BYTES + a_st;
+    const int frow = lane & 31, fkg = lane >> 5, fswz = swz(frow);
+    const uint32_t fa = (wave_m * WT_M + frow) * 128, fb = A_BYTES + (wave_n * WT_N + frow) * 128;
+
+    struct Regs {
+        u32x4 a[A_CHUNKS];
+        u32x4 b[B_CHUNKS];
+    };
+    struct Frag {
+        i32x4 a[TM], b[TN];
+    };
+
+    auto load_part = [&](Regs &g, int kt, int p) {
+#pragma unroll
+        for (int q = 0; q < A_PART; ++q) {
+            const int i = p * A_PART + q;
+            g.a[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * BK, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < B_PART; ++q) {
+            const int i = p * B_PART + q;
+            g.b[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * BK, 0);
+        }
+    };
+    auto load_all = [&](Regs &g, int kt) {
+#pragma unroll
+        for (int p = 0; p < KSUB; ++p) load_part(g, kt, p);
+    };
+    auto store_part = [&](const Regs &g, uint32_t buf, int p) {
+#pragma unroll
+        for (int q = 0; q < A_PART; ++q) {
+            const int i = p * A_PART + q;
+            *reinterpret_cast<u32x4 *>(smem + buf + a_st + i * THREADS * 16) = g.a[i];
+        }
+#pragma unroll
+        for (int q = 0; q < B_PART; ++q) {
+            const int i = p * B_PART + q;
+            *reinterpret_cast<u32x4 *>(smem + buf + b_st + i * THREADS * 16) = g.b[i];
+        }
+    };
+    auto store_all = [&](const Regs &g, uint32_t buf) {
+#pragma unroll
+        for (int p = 0; p < KSUB; ++p) store_part(g, buf, p);
+    };
+    // Fragments of substep ks: lane (row l % 32, k group l / 32) reads chunk 2 ks + l / 32.
+    auto read_frag = [&](Frag &f, uint32_t buf, int ks) {
+        const uint32_t cofs = ((2 * ks + fkg) ^ fswz) * 16;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const i32x4 *>(smem + buf + fa + cofs + i * 32 * 128);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const i32x4 *>(smem + buf + fb + cofs + j * 32 * 128);
+    };
+
+    i32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    auto mma = [&](const Frag &f) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+    };
+    constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
+
+    if (ksteps > 0) {
+        Regs R[3];
+        Frag f0, f1;
+        const int kmax = ksteps - 1;
+        // loads in the loop's own order so the loop-head wait counts stay deep
+        load_all(R[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_all(R[1], min(1, kmax));
+        __builtin_amdgcn_sched_barrier(0);
+        load_all(R[2], min(2, kmax));
+        __builtin_amdgcn_sched_barrier(0);
+        store_all(R[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_all(R[0], min(3, kmax));
+        __builtin_amdgcn_sched_barrier(0);
+        store_all(R[1], STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        load_all(R[1], min(4, kmax));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        read_frag(f0, 0, 0);
+
+        // Step k (k % 3 == J): MFMAs from stage J, step k+2's registers into
+        // stage (J+2) % 3 and reloaded with step k+5, step k+1's first
+        // fragments from stage (J+1) % 3; one barrier.
+        auto step = [&](auto J_, int kk) {
+            constexpr int J = decltype(J_)::value;
+            constexpr uint32_t cur = J * STAGE, nxt = ((J + 1) % 3) * STAGE, wr = ((J + 2) % 3) * STAGE;
+            Regs &g = R[(J + 2) % 3];
+            const int kl = min(kk + 5, kmax);
+            read_frag(f1, cur, 1);
+            store_part(g, wr, 0);
+            load_part(g, kl, 0);
+            mma(f0);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(f0, cur, 2);
+            store_part(g, wr, 1);
+            load_part(g, kl, 1);
+            mma(f1);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(f1, cur, 3);
+            store_part(g, wr, 2);
+            load_part(g, kl, 2);
+            mma(f0);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(f0, nxt, 0);
+            store_part(g, wr, 3);
+            load_part(g, kl, 3);
+            mma(f1);
+            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        int kk = 0;
+        for (; kk + 3 <= ksteps; kk += 3) {
+            step(I0{}, kk);
+            step(I1{}, kk + 1);
+            step(I2{}, kk + 2);
+        }
+        if (kk < ksteps) step(I0{}, kk);
+        if (kk + 1 < ksteps) step(I1{}, kk + 1);
+    }
+
+    if (krem) {
+        // Final partial step of krem = 32, 64 or 96 bytes: the chunks past
+        // krem are zero in LDS, so only krem / 32 substeps run.  Every wave
+        // passed the last barrier after its last LDS read, so stage 0 is free.
+        const int kt = ksteps;
+        const bool valid = (tid & 7) * 16 < krem;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (valid) v = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * BK, 0);
+            *reinterpret_cast<u32x4 *>(smem + a_st + i * THREADS * 16) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < B_CHUNKS; ++i) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (valid) v = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * BK, 0);
+            *reinterpret_cast<u32x4 *>(smem + b_st + i * THREADS * 16) = v;
+        }
+        __syncthreads();
+        for (int ks = 0; ks < krem / 32; ++ks) {
+            Frag f;
+            read_frag(f, 0, ks);
+            mma(f);
+        }
+    }
+
+    // Epilogue: tile (i, j) holds y^T -- lane l, register r is output channel
+    // 8 (r / 4) + 4 (l / 32) + r % 4 of the tile's 32, for x row l % 32.
+    // y = fp16((float(acc) * sx[row]) * sw[channel]) goes through LDS (rows
+    // padded to YS bytes) and leaves as 16-byte pieces of whole rows.
+    constexpr int YS = BN * 2 + 16;
+    static_assert(BM * YS <= kStages * STAGE, "output tile exceeds LDS");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wave_m * WT_M + i * 32 + (lane & 31);
+        const float sxv = sx[m0 + min(r, rows_m - 1)];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int c = wave_n * WT_N + j * 32 + 8 * rq + 4 * (lane >> 5);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float swv = sw[n0 + min(c + e, rows_n - 1)];
+                    v[e] = ((float)acc[i][j][4 * rq + e] * sxv) * swv;
+                }
+                const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]};
+                const f16x2 hi = {(_Float16)v[2], (_Float16)v[3]};
+                *reinterpret_cast<u32x2 *>(smem + r * YS + c * 2) = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+            }
+    }
+    __syncthreads();
+    constexpr int CPR = BN / 8;
+    constexpr int RPP = THREADS / CPR;
+    static_assert(CPR * RPP == THREADS && BM % RPP == 0, "output tile does not split evenly");
+    const bool vec16 = ((reinterpret_cast<uintptr_t>(y) & 15) == 0) && ((n_out & 7) == 0);
+    const int pc = tid % CPR, col = n0 + pc * 8;
+#pragma unroll 4
+    for (int r = tid / CPR; r < BM; r += RPP) {
+        const int row = m0 + r;
+        if (row >= m) break;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * YS + pc * 16);
+        uint16_t *yp = y + (int64_t)row * n_out + col;
+        if (vec16 && col + 8 <= n_out) {
+            *reinterpret_cast<u32x4 *>(yp) = v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (col + e < n_out) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+template <typename K>
+hipError_t allow_full_lds(K kernel)
+{
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return e;
+}
+
+template <int CPT>
+hipError_t launch_act(const uint16_t *x, const float *s, int64_t m, int k, int8_t *q, float *sx,
+                      hipStream_t stream)
+{
+    quant_act_kernel<CPT><<<(unsigned)m, kThreads, 0, stream>>>(x, s, k, q, sx);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t w8a8_launch_col_absmax(const void *src, bool f32, int64_t rows, int cols, float *out,
+                                  hipStream_t stream)
+{
+    const int cpr = cols / 8;
+    const int rows_per_block = 64;
+    const int64_t slices = (rows + rows_per_block - 1) / rows_per_block;
+    const dim3 grid((unsigned)((cpr + kThreads - 1) / kThreads), (unsigned)slices);
+    if (f32)
+        col_absmax_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, cols, rows_per_block, out);
+    else
+        col_absmax_kernel<false><<<grid, kThreads, 0, stream>>>(src, rows, cols, rows_per_block, out);
+    return hipGetLastError();
+}
+
+hipError_t w8a8_launch_smooth_factors(const float *act_max, const float *w_max, int n, float alpha, float *s,
+                                      hipStream_t stream)
+{
+    smooth_factors_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(act_max, w_max, n,
+                                                                                             alpha, s);
+    return hipGetLastError();
+}
+
+hipError_t w8a8_launch_quant_weight(const float *w, const float *s, int64_t n_out, int n_in, int8_t *q, float *sw,
+                                    hipStream_t stream)
+{
+    quant_weight_kernel<<<(unsigned)n_out, kThreads, 0, stream>>>(w, s, n_in, q, sw);
+    return hipGetLastError();
+}
+
+hipError_t w8a8_launch_quant_act(const uint16_t *x, const float *s, int64_t m, int k, int8_t *q, float *sx,
+                                 hipStream_t stream)
+{
+    const int chunks = (k / 8 + kThreads - 1) / kThreads;      // per thread
+    if (chunks <= 1) return launch_act<1>(x, s, m, k, q, sx, stream);
+    if (chunks <= 2) return launch_act<2>(x, s, m, k, q, sx, stream);
+    if (chunks <= 4) return launch_act<4>(x, s, m, k, q, sx, stream);
+    if (chunks <= 8) return launch_act<8>(x, s, m, k, q, sx, stream);
+    if (chunks <= 16) return launch_act<16>(x, s, m, k, q, sx, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t w8a8_launch_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw, int64_t m,
+                            int64_t n_out, int64_t k, uint16_t *y, hipStream_t stream)
+{
+    constexpr int BM = 256, BN = 128, WM = 4, WN = 1;
+    const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n_out + BN - 1) / BN);
+    auto kernel = w8a8_gemm_kernel<BM, BN, WM, WN>;
+    const hipError_t e = allow_full_lds(kernel);
+    if (e != hipSuccess) return e;
+    const size_t lds = kStages * (size_t)(BM + BN) * 128;
+    kernel<<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, lds, stream>>>(qx, sx, qw, sw, y, (int)m, (int)n_out,
+                                                                          (int)k, tiles_m, tiles_n);
+    return hipGetLastError();
+}
