@@ -1,5 +1,6 @@
 """CPU oracle for group-wise (or per-channel) INT4 / INT8 weight quantization,
-the W4A16 / W8A16 linear layer, the KV-cache codec and W8A8 with SmoothQuant.
+the W4A16 / W8A16 linear layer, the KV-cache codec, W8A8 with SmoothQuant,
+and GPTQ / AWQ as producers of the packed weights.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The GPU library
@@ -8,7 +9,7 @@ the arithmetic, and this module only marshals numpy arrays into it.
 
 Every function cites the passage it follows in `q4_oracle.c`.  Parity
 status: the quantizer, dequantizer, fp16 converter, reference product, KV
-codec and W8A8 path are
+codec, W8A8 path, GPTQ and AWQ are
 pinned by the CPU tests (brute force, the worked example of the interview
 guide's §3, closed forms and invariants); the packing order is this
 library's own convention (the pages give none) and is pinned only by the
@@ -64,6 +65,18 @@ class Oracle:
         lib.orc_w8a8_quant_act.restype = ctypes.c_int
         lib.orc_w8a8_quant_act.argtypes = [_p, _p, _c_i64, _c_i64, _p, _p]
         lib.orc_w8a8_gemm.argtypes = [_p, _p, _p, _p, _c_i64, _c_i64, _c_i64, _p, _p]
+        lib.orc_gptq_hessian.argtypes = [_p, _c_i64, _c_i64, _p]
+        lib.orc_gptq_damp.argtypes = [_p, _c_i64, ctypes.c_double]
+        lib.orc_gptq_hinv_chol.restype = ctypes.c_int
+        lib.orc_gptq_hinv_chol.argtypes = [_p, _c_i64, _p]
+        lib.orc_gptq_quantize.restype = ctypes.c_int
+        lib.orc_gptq_quantize.argtypes = [_p, _p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _p, _p, _p]
+        lib.orc_awq_act_mean.argtypes = [_p, _c_i64, _c_i64, _p]
+        lib.orc_awq_scales.argtypes = [_p, _c_i64, ctypes.c_double, _p]
+        lib.orc_awq_apply.restype = ctypes.c_int
+        lib.orc_awq_apply.argtypes = [_p, _p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _p, _p, _p, _p]
+        lib.orc_awq_loss.restype = ctypes.c_double
+        lib.orc_awq_loss.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64]
         lib.orc_kv_cache_bytes.restype = ctypes.c_double
         lib.orc_kv_cache_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32]
         self.lib = lib
@@ -218,6 +231,100 @@ class Oracle:
 
     def kv_cache_bytes(self, layers, kv_heads, head_dim, seq, batch, bits):
         return self.lib.orc_kv_cache_bytes(layers, kv_heads, head_dim, seq, batch, bits)
+
+    # -- GPTQ and AWQ (q4_oracle.c, "GPTQ", "AWQ") ------------------------------
+    def gptq_hessian(self, x_f16_bits):
+        """H = 2 X^T X in binary64 from fp16 calibration tokens X [t][n]."""
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        t, n = x.shape
+        h = np.empty((n, n), dtype=np.float64)
+        self.lib.orc_gptq_hessian(x.ctypes.data, t, n, h.ctypes.data)
+        return h
+
+    def gptq_damp(self, h, lam=0.01):
+        h = np.array(h, dtype=np.float64, order="C")
+        self.lib.orc_gptq_damp(h.ctypes.data, h.shape[0], float(lam))
+        return h
+
+    def gptq_hinv_chol(self, h):
+        """Upper U with U^T U = H^-1 (binary64)."""
+        h = np.ascontiguousarray(h, dtype=np.float64)
+        u = np.empty_like(h)
+        rc = self.lib.orc_gptq_hinv_chol(h.ctypes.data, h.shape[0], u.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle gptq_hinv_chol: H not positive definite" if rc == 1 else "out of memory")
+        return u
+
+    def gptq_quantize(self, w, u_f32, group_size=128, bits=4, symmetric=False):
+        """The column loop: -> (packed, scales, zeros, compensated fp32 W)."""
+        w = np.array(w, dtype=np.float32, order="C")
+        u = np.ascontiguousarray(u_f32, dtype=np.float32)
+        n_out, n = w.shape
+        g = n // group_size
+        packed = np.empty((n_out, n * bits // 32), dtype=np.uint32)
+        scales = np.empty((n_out, g), dtype=np.uint16)
+        zeros = np.empty((n_out, g), dtype=np.uint16)
+        rc = self.lib.orc_gptq_quantize(w.ctypes.data, u.ctypes.data, n_out, n, group_size, bits,
+                                        int(bool(symmetric)), packed.ctypes.data, scales.ctypes.data,
+                                        zeros.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle gptq_quantize rejected the shape")
+        return packed, scales, zeros, w
+
+    def gptq(self, w, x_f16_bits, group_size=128, bits=4, symmetric=False, lam=0.01):
+        """The whole method: Hessian, damping, U, column loop."""
+        h = self.gptq_damp(self.gptq_hessian(x_f16_bits), lam)
+        u = self.gptq_hinv_chol(h).astype(np.float32)
+        return self.gptq_quantize(w, u, group_size, bits, symmetric)[:3]
+
+    def awq_act_mean(self, x_f16_bits):
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        mean = np.empty(x.shape[1], dtype=np.float64)
+        self.lib.orc_awq_act_mean(x.ctypes.data, x.shape[0], x.shape[1], mean.ctypes.data)
+        return mean
+
+    def awq_scales(self, mean, alpha):
+        mean = np.ascontiguousarray(mean, dtype=np.float64)
+        s = np.empty(mean.size, dtype=np.float32)
+        self.lib.orc_awq_scales(mean.ctypes.data, mean.size, float(alpha), s.ctypes.data)
+        return s
+
+    def awq_apply(self, w, s, group_size=128, bits=4, symmetric=False):
+        """-> (packed, scales, zeros, effective weights dequant(Q(W diag s)) / s)."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        n_out, n = w.shape
+        g = n // group_size
+        packed = np.empty((n_out, n * bits // 32), dtype=np.uint32)
+        scales = np.empty((n_out, g), dtype=np.uint16)
+        zeros = np.empty((n_out, g), dtype=np.uint16)
+        w_eff = np.empty_like(w)
+        rc = self.lib.orc_awq_apply(w.ctypes.data, s.ctypes.data, n_out, n, group_size, bits,
+                                    int(bool(symmetric)), packed.ctypes.data, scales.ctypes.data,
+                                    zeros.ctypes.data, w_eff.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle awq_apply failed")
+        return packed, scales, zeros, w_eff
+
+    def awq_loss(self, x_f16_bits, w, w_eff):
+        x = np.ascontiguousarray(x_f16_bits, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        w_eff = np.ascontiguousarray(w_eff, dtype=np.float32)
+        return self.lib.orc_awq_loss(x.ctypes.data, x.shape[0], w.ctypes.data, w_eff.ctypes.data,
+                                     w.shape[0], w.shape[1])
+
+    def awq(self, w, x_f16_bits, group_size=128, bits=4, symmetric=False, n_grid=20):
+        """The search: -> (best alpha index, losses, s, packed, scales, zeros)."""
+        mean = self.awq_act_mean(x_f16_bits)
+        losses, best = [], None
+        for i in range(n_grid + 1):
+            s = self.awq_scales(mean, i / n_grid)
+            packed, scales, zeros, w_eff = self.awq_apply(w, s, group_size, bits, symmetric)
+            loss = self.awq_loss(x_f16_bits, w, w_eff)
+            losses.append(loss)
+            if best is None or loss < best[1]:
+                best = (i, loss, s, packed, scales, zeros)
+        return best[0], losses, best[2], best[3], best[4], best[5]
 
     # -- W8A8 with SmoothQuant (q4_oracle.c, "W8A8 with SmoothQuant") ---------
     def col_absmax_f16(self, x_f16_bits):

@@ -1,8 +1,9 @@
 /*
  * q4_oracle.c -- CPU oracle for group-wise INT4 / INT8 weight quantization
  * (per group or per output channel), the W4A16 / W8A16 linear layer, the
- * KV-cache codec (V per token, K per channel, symmetric INT8 / INT4) and the
- * W8A8 linear layer with SmoothQuant.
+ * KV-cache codec (V per token, K per channel, symmetric INT8 / INT4), the
+ * W8A8 linear layer with SmoothQuant, and GPTQ / AWQ as producers of the
+ * packed weight format.
  *
  * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct
  * definition that the GPU library is checked against.  Only the tests, the
@@ -575,4 +576,247 @@ void orc_w8a8_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const fl
             const float v = ((float)a * sx[i]) * sw[n];
             y[i * n_out + n] = orc_f32_to_f16(v);
         }
+}
+
+/* ------------------------------------------------------------------------ */
+/* GPTQ ([Guide] §4.3).                                                      */
+/* Minimize ||X W^T - X W_hat^T|| per layer: H = 2 X^T X from calibration    */
+/* tokens, damped by lambda * mean(diag H) (lambda = 0.01); the upper        */
+/* Cholesky factor U of H^-1 (U^T U = H^-1); then column by column: at each  */
+/* group start the group's scale and zero-point come from the current        */
+/* (already compensated) weights, the column is quantized, and its error     */
+/* (w - w') / U[i][i] is pushed onto every later column j as                 */
+/* w_j -= err * U[i][j].  The pages' block-128 lazy update changes only when */
+/* a column receives its corrections, not their order.                       */
+/* Readings: H, the damping and U in binary64 (H's sums run over the tokens  */
+/* in order; the diagonal mean sums in index order); U is formed without an  */
+/* explicit H^-1 -- with J the index reversal, J H J = L L^T (lower          */
+/* Cholesky) gives H = R R^T, R = J L J upper, and U = R^-1 = J L^-1 J is     */
+/* the unique upper factor with U^T U = H^-1 (pinned against that           */
+/* definition); both factorizations are right-looking, every element's       */
+/* updates applied in pivot order, one multiply and one subtract each; the   */
+/* column loop runs in binary32 with U rounded to binary32; codes use the    */
+/* fp32 scale and the error uses the stored fp16 scale (the value the        */
+/* kernels dequantize), natural column order (no activation reordering).     */
+/* ------------------------------------------------------------------------ */
+void orc_gptq_hessian(const uint16_t *x, int64_t t, int64_t n, double *h)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        for (int64_t j = 0; j <= i; j++) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < t; r++)
+                acc += (double)orc_f16_to_f32(x[r * n + i]) * (double)orc_f16_to_f32(x[r * n + j]);
+            h[i * n + j] = 2.0 * acc;
+            h[j * n + i] = 2.0 * acc;
+        }
+}
+
+void orc_gptq_damp(double *h, int64_t n, double lambda)
+{
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; i++)
+        sum += h[i * n + i];
+    const double add = lambda * (sum / (double)n);
+    for (int64_t i = 0; i < n; i++)
+        h[i * n + i] += add;
+}
+
+/* Right-looking lower Cholesky of a [n][n] (lower triangle used) in place:
+ * for each pivot j the column is scaled and the trailing lower triangle
+ * updated, a[i][k] -= l[i][j] * l[k][j].  Returns 1 if a pivot is not
+ * positive. */
+static int chol_lower_right_looking(double *a, int64_t n)
+{
+    for (int64_t j = 0; j < n; j++) {
+        if (!(a[j * n + j] > 0.0))
+            return 1;
+        const double d = sqrt(a[j * n + j]);
+        a[j * n + j] = d;
+        for (int64_t i = j + 1; i < n; i++)
+            a[i * n + j] = a[i * n + j] / d;
+        for (int64_t i = j + 1; i < n; i++)
+            for (int64_t k = j + 1; k <= i; k++)
+                a[i * n + k] = a[i * n + k] - a[i * n + j] * a[k * n + j];
+    }
+    for (int64_t i = 0; i < n; i++)
+        for (int64_t k = i + 1; k < n; k++)
+            a[i * n + k] = 0.0;
+    return 0;
+}
+
+/* M = L^-1 for lower triangular L, right-looking: B = I; for each pivot j,
+ * row j of M is B[j][.] / l[j][j] and every later row i loses
+ * l[i][j] * M[j][.]. */
+static void tri_inverse_lower_right_looking(const double *l, int64_t n, double *m)
+{
+    for (int64_t i = 0; i < n * n; i++)
+        m[i] = 0.0;
+    for (int64_t i = 0; i < n; i++)
+        m[i * n + i] = 1.0;
+    for (int64_t j = 0; j < n; j++) {
+        const double d = l[j * n + j];
+        for (int64_t c = 0; c <= j; c++)
+            m[j * n + c] = m[j * n + c] / d;
+        for (int64_t i = j + 1; i < n; i++)
+            for (int64_t c = 0; c <= j; c++)
+                m[i * n + c] = m[i * n + c] - l[i * n + j] * m[j * n + c];
+    }
+}
+
+/* U (upper, [n][n]) with U^T U = H^-1, from the damped H.  Returns 0, 1 if
+ * H is not positive definite, 2 if memory ran out. */
+int orc_gptq_hinv_chol(const double *h, int64_t n, double *u)
+{
+    double *a = (double *)malloc((size_t)(n * n) * sizeof(double));
+    double *m = (double *)malloc((size_t)(n * n) * sizeof(double));
+    if (!a || !m) {
+        free(a);
+        free(m);
+        return 2;
+    }
+    for (int64_t i = 0; i < n; i++)            /* J H J */
+        for (int64_t k = 0; k < n; k++)
+            a[i * n + k] = h[(n - 1 - i) * n + (n - 1 - k)];
+    if (chol_lower_right_looking(a, n)) {
+        free(a);
+        free(m);
+        return 1;
+    }
+    tri_inverse_lower_right_looking(a, n, m);
+    for (int64_t i = 0; i < n; i++)            /* U = J L^-1 J */
+        for (int64_t k = 0; k < n; k++)
+            u[i * n + k] = m[(n - 1 - i) * n + (n - 1 - k)];
+    free(a);
+    free(m);
+    return 0;
+}
+
+/* The column loop on w [n_out][n] (fp32, updated in place) with u [n][n]
+ * (fp32 upper factor): packed codes, fp16 scales and zeros in the library's
+ * format (as orc_quantize_pack_bits).  Returns 0, 1 for an unsupported
+ * shape, 2 if memory ran out. */
+int orc_gptq_quantize(float *w, const float *u, int64_t n_out, int64_t n, int32_t group_size,
+                      int32_t bits, int32_t symmetric, uint32_t *packed, uint16_t *scales,
+                      uint16_t *zeros)
+{
+    if ((bits != 4 && bits != 8) || group_size <= 0 || n % group_size != 0 || n % (32 / bits) != 0)
+        return 1;
+    const int per_word = 32 / bits;
+    const int64_t words = n / per_word, groups = n / group_size;
+    const int32_t offset = 1 << (bits - 1);
+    const float top = symmetric ? (float)(offset - 1) : (float)((1 << bits) - 1);
+    const float bottom = symmetric ? -(float)offset : 0.0f;
+    int failed = 0;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_out; r++) {
+        int32_t *codes = (int32_t *)malloc((size_t)group_size * sizeof(int32_t));
+        if (!codes) {
+            #pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        float *row = w + r * n;
+        uint32_t *prow = packed + r * words;
+        memset(prow, 0, (size_t)words * sizeof(uint32_t));
+        float s = 1.0f, s16 = 1.0f;
+        int32_t z = 0;
+        for (int64_t i = 0; i < n; i++) {
+            if (i % group_size == 0) {
+                orc_quantize_group(row + i, group_size, bits, symmetric, &s, &z, codes);
+                const uint16_t sh = orc_f32_to_f16(s);
+                s16 = orc_f16_to_f32(sh);
+                scales[r * groups + i / group_size] = sh;
+                zeros[r * groups + i / group_size] = orc_f32_to_f16((float)(symmetric ? offset : z));
+            }
+            const float q = clampf(rintf(row[i] / s) + (float)z, bottom, top);
+            const float deq = s16 * (q - (float)z);
+            const float err = (row[i] - deq) / u[i * n + i];
+            const uint32_t code = (uint32_t)(int32_t)(symmetric ? q + (float)offset : q);
+            prow[i / per_word] |= code << (bits * (i % per_word));
+            for (int64_t j = i + 1; j < n; j++)
+                row[j] = row[j] - err * u[i * n + j];
+        }
+        free(codes);
+    }
+    return failed ? 2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* AWQ ([Guide] §4.4).                                                       */
+/* Per input channel s_j = (mean_t |X_tj|)^alpha; the weights are scaled by  */
+/* s, quantized group-wise, and the activation is divided by s at run time   */
+/* (so the effective weight is dequant(Q(W diag(s))) / s); alpha is searched */
+/* on a grid over [0, 1] for the smallest reconstruction error of the        */
+/* layer output on the calibration tokens.                                   */
+/* Readings: the mean of |x| sums the tokens in order in binary64; s =       */
+/* float(pow(mean, alpha)) floored at 1e-5 (the SmoothQuant listing's       */
+/* floor); W * s and dequant / s in binary32; the error is                   */
+/* sum_t sum_n (sum_k x_tk (w_nk - w_eff_nk))^2 in binary64, each inner sum   */
+/* over k in order, the outer sums over t then n in order; the grid is       */
+/* alpha = i / n_grid, i = 0..n_grid, and the first smallest error wins.     */
+/* ------------------------------------------------------------------------ */
+void orc_awq_act_mean(const uint16_t *x, int64_t t, int64_t n, double *mean)
+{
+    for (int64_t j = 0; j < n; j++) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < t; r++)
+            acc += fabs((double)orc_f16_to_f32(x[r * n + j]));
+        mean[j] = acc / (double)t;
+    }
+}
+
+void orc_awq_scales(const double *mean, int64_t n, double alpha, float *s)
+{
+    for (int64_t j = 0; j < n; j++) {
+        const float v = (float)pow(mean[j], alpha);
+        s[j] = v < 1e-5f ? 1e-5f : v;
+    }
+}
+
+/* Effective weights of one alpha: w_eff = dequant(Q(W diag(s))) / s, with
+ * the packed result of Q written out. */
+int orc_awq_apply(const float *w, const float *s, int64_t n_out, int64_t n, int32_t group_size,
+                  int32_t bits, int32_t symmetric, uint32_t *packed, uint16_t *scales,
+                  uint16_t *zeros, float *w_eff)
+{
+    float *ws = (float *)calloc((size_t)(n_out * n), sizeof(float));
+    if (!ws)
+        return 2;
+    for (int64_t r = 0; r < n_out; r++)
+        for (int64_t k = 0; k < n; k++)
+            ws[r * n + k] = w[r * n + k] * s[k];
+    int rc = orc_quantize_pack_bits(ws, n_out, n, group_size, bits, symmetric, packed, scales, zeros, NULL);
+    if (rc == 0) {
+        orc_dequant_bits(packed, scales, zeros, n_out, n, group_size, bits, ws);
+        for (int64_t r = 0; r < n_out; r++)
+            for (int64_t k = 0; k < n; k++)
+                w_eff[r * n + k] = ws[r * n + k] / s[k];
+    }
+    free(ws);
+    return rc;
+}
+
+double orc_awq_loss(const uint16_t *x, int64_t t, const float *w, const float *w_eff, int64_t n_out, int64_t n)
+{
+    double *part = (double *)malloc((size_t)n_out * sizeof(double));
+    if (!part)
+        return -1.0;
+    #pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < n_out; c++) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < t; r++) {
+            double y = 0.0;
+            for (int64_t k = 0; k < n; k++)
+                y += (double)orc_f16_to_f32(x[r * n + k]) *
+                     ((double)w[c * n + k] - (double)w_eff[c * n + k]);
+            acc += y * y;
+        }
+        part[c] = acc;
+    }
+    double total = 0.0;
+    for (int64_t c = 0; c < n_out; c++)
+        total += part[c];
+    free(part);
+    return total;
 }

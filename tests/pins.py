@@ -664,6 +664,131 @@ def pin_w8a8_error_bound(orc, quick=False):
         assert np.abs(yf - ref).max() < err0, "smoothing should reduce the error on outlier activations"
 
 
+# ---------------------------------------------------------------------------
+# GPTQ (the interview guide's §4.3) and AWQ (§4.4).
+# ---------------------------------------------------------------------------
+def _calib(t, n, seed, outliers=2):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((t, n)).astype(np.float32)
+    x[:, rng.choice(n, outliers, replace=False)] *= 8.0
+    return x.astype(np.float16)
+
+
+def _out_err(x, w, wd):
+    xf = x.astype(np.float64)
+    return float(np.sum((xf @ (w.astype(np.float64) - wd.astype(np.float64)).T) ** 2))
+
+
+def pin_gptq_hessian_and_factor(orc, quick=False):
+    """H = 2 X^T X, the damping adds 0.01 mean(diag H) to the diagonal, and U
+    is upper triangular with a positive diagonal and U^T U = H^-1, which by
+    uniqueness of the Cholesky factor makes it the factor the method names."""
+    x = _calib(300, 96, 91)
+    h = orc.gptq_hessian(x.view(np.uint16))
+    xf = x.astype(np.float64)
+    np.testing.assert_allclose(h, 2.0 * xf.T @ xf, rtol=1e-13, atol=1e-9)
+    hd = orc.gptq_damp(h, 0.01)
+    want = h + np.eye(96) * 0.01 * np.mean(np.diag(h))
+    np.testing.assert_allclose(hd, want, rtol=1e-14)
+    u = orc.gptq_hinv_chol(hd)
+    assert np.array_equal(u, np.triu(u)) and (np.diag(u) > 0).all()
+    hinv = np.linalg.inv(hd)
+    np.testing.assert_allclose(u.T @ u, hinv, rtol=1e-9, atol=1e-12 * np.abs(hinv).max())
+
+
+def pin_gptq_diagonal_hessian_is_rounding(orc, quick=False):
+    """With a diagonal H the factor is diagonal, no error reaches another
+    column, and GPTQ is plain round-to-nearest with the same groups."""
+    w = synthetic.normal_weight(8, 256, seed=92, n_outlier_cols=2)
+    u = np.diag(np.random.default_rng(93).uniform(0.5, 2.0, 256)).astype(np.float32)
+    for g in (32, 128):
+        for sym in (False, True):
+            p, sc, z, _ = orc.gptq_quantize(w, u, g, 4, sym)
+            pr, scr, zr, _ = orc.quantize_pack(w, g, sym)
+            assert np.array_equal(p, pr) and np.array_equal(sc, scr) and np.array_equal(z, zr), (g, sym)
+
+
+def _obq(w, hinv, g, bits=4):
+    """The guide's OBQ statement, independently of the Cholesky form: for
+    each column q the rest moves by -(w_q - quant(w_q)) / Hinv_qq * Hinv_q,rest,
+    then q is eliminated from Hinv.  Group parameters come from the current
+    weights with the asymmetric binary32 map; the error uses the fp16-stored
+    scale.  Returns the codes and the compensated weights (binary64)."""
+    w = w.astype(np.float64).copy()
+    hinv = hinv.copy()
+    n_out, n = w.shape
+    codes = np.zeros((n_out, n), dtype=np.int64)
+    s = np.zeros(n_out, dtype=np.float32)
+    zz = np.zeros(n_out, dtype=np.int64)
+    qmax = (1 << bits) - 1
+    for q in range(n):
+        for r in range(n_out):
+            if q % g == 0:
+                grp = w[r, q:q + g].astype(np.float32)
+                mn, mx = np.float32(grp.min()), np.float32(grp.max())
+                sc = max(np.float32((mx - mn) / np.float32(qmax)), np.float32(1e-8))
+                s[r] = sc
+                zz[r] = int(min(max(np.rint(np.float32(-mn / sc)), 0), qmax))
+            c = int(min(max(np.rint(np.float32(np.float32(w[r, q]) / s[r])) + zz[r], 0), qmax))
+            codes[r, q] = c
+            deq = float(np.float16(s[r])) * (c - zz[r])
+            e = (w[r, q] - deq) / hinv[q, q]
+            w[r, q + 1:] -= e * hinv[q, q + 1:]
+        hinv = hinv - np.outer(hinv[:, q], hinv[q, :]) / hinv[q, q]
+    return codes, w
+
+
+def pin_gptq_matches_obq(orc, quick=False):
+    """Codes and compensated weights of the Cholesky-form column loop equal
+    those of the explicit OBQ elimination (binary32 against binary64)."""
+    rng = np.random.default_rng(94)
+    w = (rng.standard_normal((4, 32)) * 0.02).astype(np.float32)
+    x = _calib(200, 32, 95)
+    h = orc.gptq_damp(orc.gptq_hessian(x.view(np.uint16)), 0.01)
+    u = orc.gptq_hinv_chol(h).astype(np.float32)
+    packed, _, _, w_comp = orc.gptq_quantize(w, u, 16, 4, False)
+    codes = np.array([[(int(packed[r, k // 8]) >> (4 * (k % 8))) & 15 for k in range(32)] for r in range(4)])
+    want_codes, want_w = _obq(w, np.linalg.inv(h), 16)
+    assert np.array_equal(codes, want_codes), "codes differ from the OBQ elimination"
+    scale = np.abs(w).max()
+    assert np.abs(w_comp - want_w).max() <= 2e-5 * scale, np.abs(w_comp - want_w).max() / scale
+
+
+def pin_gptq_lowers_output_error(orc, quick=False):
+    for seed in (96, 97):
+        w = synthetic.normal_weight(32, 256, seed=seed, n_outlier_cols=2)
+        x = _calib(400, 256, seed + 10)
+        for g in (32, 128):
+            p, sc, z = orc.gptq(w, x.view(np.uint16), g)
+            pr, scr, zr, _ = orc.quantize_pack(w, g)
+            e_g = _out_err(x, w, orc.dequant(p, sc, z, g))
+            e_r = _out_err(x, w, orc.dequant(pr, scr, zr, g))
+            assert e_g < e_r, f"seed {seed} g={g}: GPTQ {e_g:.4g} vs rounding {e_r:.4g}"
+
+
+def pin_awq(orc, quick=False):
+    w = synthetic.normal_weight(24, 256, seed=98, n_outlier_cols=0)
+    x = _calib(128, 256, 99, outliers=6)
+    mean = orc.awq_act_mean(x.view(np.uint16))
+    np.testing.assert_allclose(mean, np.abs(x.astype(np.float64)).mean(axis=0), rtol=1e-15)
+    s = orc.awq_scales(mean, 0.5)
+    np.testing.assert_allclose(s, np.maximum(mean ** 0.5, 1e-5), rtol=1e-7)
+    assert (orc.awq_scales(np.zeros(3), 0.5) == np.float32(1e-5)).all()
+    # alpha = 0: s = 1 and AWQ is plain rounding
+    p0, s0, z0, w_eff0 = orc.awq_apply(w, orc.awq_scales(mean, 0.0), 128)
+    pr, sr, zr, _ = orc.quantize_pack(w, 128)
+    assert np.array_equal(p0, pr) and np.array_equal(s0, sr) and np.array_equal(z0, zr)
+    # the loss is the squared output error on the calibration tokens
+    p, sc, z, w_eff = orc.awq_apply(w, s, 128)
+    loss = orc.awq_loss(x.view(np.uint16), w, w_eff)
+    np.testing.assert_allclose(loss, _out_err(x, w, w_eff), rtol=1e-10)
+    # and w_eff is the dequantized W diag(s) divided back by s
+    np.testing.assert_allclose(w_eff * s[None, :], orc.dequant(p, sc, z, 128), rtol=2e-7, atol=1e-12)
+    best, losses, s_b, *_ = orc.awq(w, x.view(np.uint16), 128)
+    assert losses[best] == min(losses) and best == int(np.argmin(losses))
+    assert losses[best] < losses[0], "scaling the salient channels should beat plain rounding here"
+
+
 ALL_PINS = [
     pin_worked_example, pin_brute_force, pin_ties_to_even, pin_zero_clip,
     pin_reconstruction_bound, pin_idempotence, pin_grid_exact, pin_constant_groups,
@@ -673,4 +798,6 @@ ALL_PINS = [
     pin_kv_brute_force, pin_kv_worked_example, pin_kv_transpose, pin_kv_bound, pin_kv_ties_and_zero,
     pin_kv_cache_sizes,
     pin_sq_balance_and_limits, pin_sq_clamps, pin_w8a8_row_quantizers, pin_w8a8_gemm, pin_w8a8_error_bound,
+    pin_gptq_hessian_and_factor, pin_gptq_diagonal_hessian_is_rounding, pin_gptq_matches_obq,
+    pin_gptq_lowers_output_error, pin_awq,
 ]

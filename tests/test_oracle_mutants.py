@@ -68,6 +68,17 @@ MUTANTS = {
                                  "const float v = ((float)a * sw[n]) * sw[n];"),
     "w8a8_gemm_k_shift": ("a += (int64_t)qx[i * k + j] * (int64_t)qw[n * k + j];",
                           "a += (int64_t)qx[i * k + j] * (int64_t)qw[n * k + (j + 1) % k];"),
+    "gptq_hessian_not_doubled": ("            h[i * n + j] = 2.0 * acc;\n            h[j * n + i] = 2.0 * acc;",
+                                 "            h[i * n + j] = acc;\n            h[j * n + i] = acc;"),
+    "gptq_damp_sum_not_mean": ("const double add = lambda * (sum / (double)n);", "const double add = lambda * sum;"),
+    "gptq_factor_not_reversed": ("a[i * n + k] = h[(n - 1 - i) * n + (n - 1 - k)];", "a[i * n + k] = h[i * n + k];"),
+    "gptq_error_undivided": ("const float err = (row[i] - deq) / u[i * n + i];", "const float err = row[i] - deq;"),
+    "gptq_update_sign": ("row[j] = row[j] - err * u[i * n + j];", "row[j] = row[j] + err * u[i * n + j];"),
+    "gptq_error_fp32_scale": ("const float deq = s16 * (q - (float)z);", "const float deq = s * (q - (float)z) * 1.001f;"),
+    "awq_mean_signed": ("acc += fabs((double)orc_f16_to_f32(x[r * n + j]));", "acc += (double)orc_f16_to_f32(x[r * n + j]);"),
+    "awq_alpha_complement": ("const float v = (float)pow(mean[j], alpha);", "const float v = (float)pow(mean[j], 1.0 - alpha);"),
+    "awq_eff_multiplied": ("w_eff[r * n + k] = ws[r * n + k] / s[k];", "w_eff[r * n + k] = ws[r * n + k] * s[k];"),
+    "awq_loss_unsquared": ("acc += y * y;", "acc += fabs(y);"),
 }
 
 
