@@ -14,7 +14,7 @@ from w4a16_dequant_gemv_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
-HEADERS = [HEADER, os.path.join(ROOT, "include", "kv_codec.h"), os.path.join(ROOT, "include", "w8a8.h")]
+HEADERS = [HEADER] + [os.path.join(ROOT, "include", h) for h in ("kv_codec.h", "w8a8.h", "producers.h")]
 
 P16 = 0x10000      # 16-byte aligned placeholder address (never dereferenced)
 P2 = 0x10002       # 2-byte but not 16-byte aligned
@@ -24,7 +24,8 @@ def header_functions():
     names = set()
     for h in HEADERS:
         text = open(h, encoding="utf-8").read()
-        names |= set(re.findall(r"^\s*(?:int|const char \*)\s*((?:q[48]|kv|sq|w8a8)_\w+)\s*\(", text, re.M))
+        names |= set(re.findall(r"^\s*(?:int64_t|int|const char \*)\s*((?:q[48]|kv|sq|w8a8|gptq|awq)_\w+)\s*\(",
+                                text, re.M))
     return sorted(names)
 
 
@@ -257,3 +258,22 @@ def test_w8a8_rejects(L):
     assert L.w8a8_gemm(P16 + 8, P16, P16, P16, 4, 8, 64, P16, None) == _lib.Q4_ERR_ALIGN
     assert L.w8a8_gemm(P16, P16, P16, P16, 4, 8, 64, P16 + 1, None) == _lib.Q4_ERR_ALIGN
     assert L.w8a8_gemm(P16, None, P16, P16, 4, 8, 64, P16, None) == _lib.Q4_ERR_NULL
+
+
+def test_producers_reject(L):
+    assert L.gptq_factor_workspace_size(256) == 2 * 256 * 256 * 8
+    assert L.gptq_hinv_factor(P16, 64, 256, 0.01, None, 1 << 20, P16, None) == _lib.Q4_ERR_NULL
+    assert L.gptq_hinv_factor(P16, 64, 100, 0.01, P16, 1 << 20, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.gptq_hinv_factor(P16, 64, 256, 0.01, P16, 1000, P16, None) == _lib.Q4_ERR_SHAPE   # workspace too small
+    assert L.gptq_hinv_factor(P16, 64, 256, -1.0, P16, 1 << 20, P16, None) == _lib.Q4_ERR_SHAPE
+    assert L.gptq_hinv_factor(P16, 64, 256, 0.01, P16 + 16, 1 << 20, P16, None) == _lib.Q4_ERR_ALIGN
+    ws = L.gptq_quantize_workspace_size(8, 256)
+    assert L.gptq_quantize(P16, P16, 8, 256, 48, 4, 0, P16, ws, P16, P2, P2, None) == _lib.Q4_ERR_GROUP
+    assert L.gptq_quantize(P16, P16, 8, 256, 128, 3, 0, P16, ws, P16, P2, P2, None) == _lib.Q4_ERR_SHAPE
+    assert L.gptq_quantize(P16, P16, 8, 256, 128, 4, 0, P16, ws - 1, P16, P2, P2, None) == _lib.Q4_ERR_SHAPE
+    assert L.gptq_quantize(P16, P16, 8, 256, 128, 4, 0, P16, ws, P16 + 4, P2, P2, None) == _lib.Q4_ERR_ALIGN
+    wa = L.awq_workspace_size(8, 256, 64, 20, 128)
+    assert wa > 0
+    assert L.awq_quantize(P16, P16, 64, 8, 256, 128, 4, 0, 0, P16, wa, P16, P2, P2, P16, None, None, None) == _lib.Q4_ERR_SHAPE
+    assert L.awq_quantize(P16, P16, 64, 8, 256, 128, 4, 0, 20, P16, wa - 1, P16, P2, P2, P16, None, None, None) == _lib.Q4_ERR_SHAPE
+    assert L.awq_quantize(P16, P16, 64, 8, 256, 128, 4, 0, 20, P16, wa, P16, P2, P2, None, None, None, None) == _lib.Q4_ERR_NULL

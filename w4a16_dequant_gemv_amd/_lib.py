@@ -36,6 +36,13 @@ SIGNATURES = {
     "w8a8_quantize_weight": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p]),
     "w8a8_quantize_act": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p]),
     "w8a8_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p]),
+    "gptq_factor_workspace_size": (_i64, [_i64]),
+    "gptq_hinv_factor": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_double, _p, _i64, _p, _p]),
+    "gptq_quantize_workspace_size": (_i64, [_i64, _i64]),
+    "gptq_quantize": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
+    "awq_workspace_size": (_i64, [_i64, _i64, _i64, _i32, _i32]),
+    "awq_quantize": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _i64, _p, _p, _p, _p,
+                                    _p, _p, _p]),
 }
 
 

@@ -3,7 +3,8 @@
     python -m w4a16_dequant_gemv_amd.build
 
 Every translation unit is compiled with packed-fp32 instruction selection
-disabled; the weight quantizer's, the KV codec's and the W8A8 units additionally keep
+disabled; the weight quantizer's, the KV codec's, the W8A8 and the GPTQ/AWQ units
+additionally keep
 each fp32 operation separate (no FMA contraction) and use correctly rounded
 fp32 division, which their bit-exactness depends on.
 """
@@ -30,8 +31,10 @@ PER_FILE = {
     "q4_quantize.hip": EXACT_FP32,
     "kv_codec.hip": EXACT_FP32,
     "w8a8.hip": EXACT_FP32,
+    "producers.hip": EXACT_FP32,
 }
-SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip", "kv_codec.hip", "w8a8.hip"]
+SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip", "kv_codec.hip", "w8a8.hip",
+           "producers.hip"]
 
 
 def _compile(src):

@@ -3,6 +3,7 @@
 #include "w4a16.h"
 #include "kv_codec.h"
 #include "w8a8.h"
+#include "producers.h"
 
 #include "q4_launch.h"
 
@@ -63,6 +64,15 @@ int check_linear(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 int check_w8a8_k(int64_t k) { return (k >= 32 && k <= 32768 && k % 32 == 0) ? Q4_OK : Q4_ERR_SHAPE; }
 
 int check_rows(int64_t r) { return (r >= 1 && r <= kMaxRows) ? Q4_OK : Q4_ERR_SHAPE; }
+
+// GPTQ / AWQ shapes: n a multiple of 32 in [32, 32768], the weight group rules.
+int check_producer(int64_t n_out, int64_t n, int32_t group_size, int32_t bits)
+{
+    if (n < 32 || n > 32768 || n % 32 != 0 || check_rows(n_out) || n_out * n > kMaxElems) return Q4_ERR_SHAPE;
+    if (bits != 4 && bits != 8) return Q4_ERR_SHAPE;
+    if (int rc = check_group(group_size, n)) return rc;
+    return n % group_size == 0 ? Q4_OK : Q4_ERR_SHAPE;
+}
 
 // KV codec shapes: head dimension d a multiple of 8 in [8, 512]; per-channel
 // blocks of t tokens fit 32 rows per thread (t <= 32 * (2048 / d)).
@@ -313,6 +323,62 @@ int w8a8_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const float *
     if (!aligned(qx, 16) || !aligned(qw, 16) || !aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 2))
         return Q4_ERR_ALIGN;
     return finish(w8a8_launch_gemm(qx, sx, qw, sw, m, n_out, k, y, (hipStream_t)stream));
+}
+
+int64_t gptq_factor_workspace_size(int64_t n) { return n > 0 ? gptq_factor_workspace(n) : 0; }
+
+int64_t gptq_quantize_workspace_size(int64_t n_out, int64_t n)
+{
+    return (n_out > 0 && n > 0) ? gptq_loop_workspace(n_out, n) : 0;
+}
+
+int64_t awq_workspace_size(int64_t n_out, int64_t n, int64_t tokens, int32_t n_grid, int32_t group_size)
+{
+    if (n_out <= 0 || n <= 0 || tokens <= 0 || n_grid <= 0 || group_size <= 0) return 0;
+    return awq_workspace(n_out, n, tokens, n_grid, group_size);
+}
+
+int gptq_hinv_factor(const uint16_t *x, int64_t tokens, int64_t n, double damp, void *workspace,
+                     int64_t workspace_bytes, float *u, void *stream)
+{
+    if (!x || !workspace || !u) return Q4_ERR_NULL;
+    if (n < 32 || n > 32768 || n % 32 != 0 || check_rows(tokens) || tokens * n > kMaxElems) return Q4_ERR_SHAPE;
+    if (!(damp >= 0.0 && damp < 1e6)) return Q4_ERR_SHAPE;
+    if (workspace_bytes < gptq_factor_workspace(n)) return Q4_ERR_SHAPE;
+    if (!aligned(x, 2) || !aligned(workspace, 256) || !aligned(u, 4)) return Q4_ERR_ALIGN;
+    return finish(gptq_launch_factor(x, tokens, (int)n, damp, workspace, u, (hipStream_t)stream));
+}
+
+int gptq_quantize(const float *w, const float *u, int64_t n_out, int64_t n, int32_t group_size,
+                  int32_t bits, int32_t symmetric, void *workspace, int64_t workspace_bytes,
+                  uint32_t *qweight, uint16_t *scales, uint16_t *zeros, void *stream)
+{
+    if (!w || !u || !workspace || !qweight || !scales || !zeros) return Q4_ERR_NULL;
+    if (int rc = check_producer(n_out, n, group_size, bits)) return rc;
+    if (workspace_bytes < gptq_loop_workspace(n_out, n)) return Q4_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(u, 4) || !aligned(workspace, 256) || !aligned(qweight, 16) ||
+        !aligned(scales, 2) || !aligned(zeros, 2))
+        return Q4_ERR_ALIGN;
+    return finish(gptq_launch_loop(w, u, n_out, (int)n, group_size, bits, symmetric != 0, workspace, qweight,
+                                   scales, zeros, (hipStream_t)stream));
+}
+
+int awq_quantize(const float *w, const uint16_t *x, int64_t tokens, int64_t n_out, int64_t n,
+                 int32_t group_size, int32_t bits, int32_t symmetric, int32_t n_grid, void *workspace,
+                 int64_t workspace_bytes, uint32_t *qweight, uint16_t *scales, uint16_t *zeros, float *s,
+                 int32_t *best, float *losses, void *stream)
+{
+    if (!w || !x || !workspace || !qweight || !scales || !zeros || !s) return Q4_ERR_NULL;
+    if (int rc = check_producer(n_out, n, group_size, bits)) return rc;
+    if (check_rows(tokens) || tokens * n > kMaxElems || tokens * n_out > kMaxElems) return Q4_ERR_SHAPE;
+    if (n_grid < 1 || n_grid > 100) return Q4_ERR_SHAPE;
+    if (workspace_bytes < awq_workspace(n_out, n, tokens, n_grid, group_size)) return Q4_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(x, 2) || !aligned(workspace, 256) || !aligned(qweight, 16) ||
+        !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(s, 4) || (best && !aligned(best, 4)) ||
+        (losses && !aligned(losses, 4)))
+        return Q4_ERR_ALIGN;
+    return finish(awq_launch(w, x, tokens, n_out, (int)n, group_size, bits, symmetric != 0, n_grid, workspace,
+                             qweight, scales, zeros, s, best, losses, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -46,3 +46,16 @@ hipError_t w8a8_launch_quant_act(const uint16_t *x, const float *s, int64_t m, i
                                  hipStream_t stream);
 hipError_t w8a8_launch_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw, int64_t m,
                             int64_t n_out, int64_t k, uint16_t *y, hipStream_t stream);
+
+// GPTQ and AWQ (producers.hip).  Workspace sizes in bytes.
+int64_t gptq_factor_workspace(int64_t n);
+int64_t gptq_loop_workspace(int64_t n_out, int64_t n);
+int64_t awq_workspace(int64_t n_out, int64_t n, int64_t t, int n_grid, int group_size);
+hipError_t gptq_launch_factor(const uint16_t *x, int64_t t, int n, double damp, void *workspace, float *u,
+                              hipStream_t stream);
+hipError_t gptq_launch_loop(const float *w, const float *u, int64_t n_out, int n, int group_size, int bits,
+                            bool symmetric, void *workspace, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                            hipStream_t stream);
+hipError_t awq_launch(const float *w, const uint16_t *x, int64_t t, int64_t n_out, int n, int group_size, int bits,
+                      bool symmetric, int n_grid, void *workspace, uint32_t *qweight, uint16_t *scales,
+                      uint16_t *zeros, float *s_out, int32_t *best_out, float *losses_out, hipStream_t stream);
