@@ -21,6 +21,8 @@ Also measured in the same run and reported as extra keys:
               decode-time flush of 256 window blocks into a block pool,
   w8a8_smoothquant -- the int8 product at m=2048 on the 7B shapes (TOP/s) and
               the whole smoothed layer (activation quantization + product),
+  gptq_awq -- GPTQ and AWQ on one 4096x4096 linear: time per layer and the
+              output error relative to plain rounding,
   cpu_baseline -- the CPU oracle (dequantize + binary64 product) timed on
                   this host's cores on a bounded sample of the decode step.
 
@@ -449,6 +451,49 @@ def bench_w8a8(args, dev):
                 layer_tops=round(tot_op / tot_layer_t / 1e12, 1))
 
 
+def bench_producers(args, dev):
+    """GPTQ (512 calibration tokens) and AWQ (128 tokens, 21-point grid) on one
+    4096x4096 linear, INT4 g=128: wall time per layer on the GPU and each
+    method's output error on its calibration tokens relative to plain
+    rounding (the quantity both methods minimize)."""
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    from w4a16_dequant_gemv_amd import producers, synthetic as syn
+    n = 4096
+    w = syn.normal_weight_device(n, n, 4300, 0.02, syn.n_outliers(n), dev)
+    x = syn.activations_f16_device(512, n, 4301, dev)
+    x[:, :8] *= 8                      # a few outlier activation channels
+    res = {}
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = fn()
+        torch.cuda.synchronize()
+        return out, time.perf_counter() - t0
+
+    producers.gptq(w[:256], x[:64], 128)           # warm the launch paths
+    u, t_fac = timed(lambda: producers.gptq_factor(x))
+    g, t_loop = timed(lambda: producers.gptq_quantize(w, u, 128))
+    xa = x[:128].contiguous()
+    (qa, s_awq, best, losses), t_awq = timed(lambda: producers.awq(w, xa, 128))
+    r = w4.quantize_pack(w, 128)
+
+    def out_err(xx, wd):
+        return ((xx.double() @ (w.double() - wd.double()).t()) ** 2).sum().item()
+
+    e_r = out_err(x, w4.dequant(r))
+    res["gptq"] = dict(tokens=512, factor_ms=round(t_fac * 1e3, 1), loop_ms=round(t_loop * 1e3, 1),
+                       err_vs_rounding=round(out_err(x, w4.dequant(g)) / e_r, 4))
+    e_ra = out_err(xa, w4.dequant(r))
+    eff = w4.dequant(qa) / s_awq[None, :]
+    res["awq"] = dict(tokens=128, grid=20, ms=round(t_awq * 1e3, 1), alpha=round(int(best.item()) / 20, 2),
+                      err_vs_rounding=round(out_err(xa, eff) / e_ra, 4))
+    del w, x, u, g, r, qa
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_stress_and_quantize(args, dev):
     import torch
     import w4a16_dequant_gemv_amd as w4
@@ -554,6 +599,8 @@ def main():
         log(f"kv codec: {extras['kv']}")
         extras["w8a8"] = bench_w8a8(args, dev)
         log(f"w8a8: {extras['w8a8']}")
+        extras["producers"] = bench_producers(args, dev)
+        log(f"gptq/awq: {extras['producers']}")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host_w, args.cpu_seconds)
@@ -599,6 +646,7 @@ def main():
         record["w8a16"] = extras["int8"]
         record["kv_codec"] = extras["kv"]
         record["w8a8_smoothquant"] = extras["w8a8"]
+        record["gptq_awq"] = extras["producers"]
     print(json.dumps(record), flush=True)
 
 
