@@ -12,19 +12,24 @@
 // Warp specialization.  The workgroup has eight waves, two per SIMD: four
 // consumers, each owning BM/4 x BN of the tile as 32x32 MFMA tiles, whose
 // instruction streams are only LDS fragment reads and MFMAs; and four
-// producers, which load the x chunks and packed words from global memory,
-// dequantize the weights to fp16 s * (c - z) and write both into LDS.  The
-// SIMD interleaves the two waves it holds, so the dequantization arithmetic
-// and the global-load waits of the producer overlap the consumer's MFMAs
-// without sharing one instruction stream.
+// producers, which bring x and the packed weights of each step into LDS,
+// the weights dequantized to fp16 s * (c - z).  The SIMD interleaves the
+// two waves it holds, so the dequantization arithmetic and the load waits
+// of the producer overlap the consumer's MFMAs without sharing one
+// instruction stream.
 //
 // Pipeline.  Three LDS stages; one barrier per step, shared by both roles:
 //   * consumers compute step k from stage k%3 (two fragment register sets,
 //     substep s+1's fragments read while substep s runs its MFMAs) and read
 //     step k+1's first fragments from stage (k+1)%3 before the barrier;
-//   * producers write step k+2 into stage (k+2)%3 from one of three
-//     register sets and reload that set with step k+5's data, so every
-//     global load has about three steps to arrive.
+//   * producers fill stage (k+2)%3 during step k: x by direct global->LDS
+//     loads (buffer_load ... lds: no registers, no LDS store instructions,
+//     which gfx950 executes at well under half its LDS read rate), weights
+//     from one of three register sets loaded three steps earlier, which is
+//     then reloaded with step k+5.  Before the barrier a producer waits
+//     only until the step's x loads (and every older load) have landed,
+//     leaving the new weight loads in flight; a barrier that waited for
+//     every load would empty the pipeline each step.
 // Both rotations have period three, so the loop is unrolled three times and
 // every LDS address is a lane constant plus an immediate.  Global loads are
 // buffer loads: a per-tile resource, a lane-constant 32-bit offset and a
@@ -88,6 +93,28 @@ __device__ __forceinline__ u32x2 dequant_byte_word(uint32_t w, f16x2 bias, f16x2
 constexpr int kConsumers = 4, kProducers = 4;
 constexpr int kGemmThreads = 64 * (kConsumers + kProducers);
 
+// Wait until at most N vector-memory operations of this wave are
+// outstanding; the empty asm statements keep the compiler from moving
+// memory accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem()
+{
+    static_assert(N >= 0 && N < 64, "the vector-memory counter has six bits");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only, leaving
+// its vector-memory loads in flight.
+__device__ __forceinline__ void barrier_keep_vmem()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // PAIR_SZ: the two lanes of each lane pair dequantize slices of the same
 // row and group (every case but INT4 with groups of 32), so the even lane
 // loads the scale, the odd lane the zero-point, and a DPP swap gives each
@@ -106,12 +133,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     // A 16-byte slice of packed codes holds 128/BITS codes (32 INT4, 16 INT8),
     // i.e. CHS fp16 LDS chunks; a row's 64 codes per step are SPR slices.
     constexpr int SPR = BITS / 2, CPS = 128 / BITS, CHS = CPS / 8;
-    constexpr int A_CHUNKS = BM * 8 / PT;               // 16-byte x chunks per producer lane per step
+    constexpr int A_CHUNKS = BM * 8 / PT;               // 16-byte x chunks per producer lane (32-wide tail step)
     constexpr int B_SLICES = BN * SPR / PT;             // 16-byte code slices per producer lane per step
     static_assert(A_CHUNKS * PT == BM * 8, "x tile does not split evenly");
     static_assert(B_SLICES * PT == BN * SPR, "weight tile does not split evenly");
     static_assert(TM * 32 == WT_M && TN * 32 == WT_N, "wave tile not a multiple of 32");
     static_assert(PT % 128 == 0 && (PT / SPR) % 16 == 0, "row swizzles assume 16-row lane strides");
+    static_assert(BM == 64 * kProducers, "each producer wave loads 64 rows of x per step");
     constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
     static_assert(kStages == 3, "the loop is unrolled for three stages");
     static_assert(kStages * STAGE <= 160 * 1024, "stages exceed LDS");
@@ -247,9 +275,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
             soff[i] = ((uint32_t)r * (uint32_t)groups_per_row + (uint32_t)(((c % SPR) * CPS) >> group_shift)) * 2u;
             szp[i] = reinterpret_cast<const uint16_t *>(((c & 1) ? zg : sg) + soff[i]);
         }
-        // LDS byte offsets within a stage: x chunk i of this lane, weight
-        // chunk j of slice i.  Rows of chunk (slice) i differ by multiples of
-        // 16 from those of chunk (slice) 0, so they share its swizzle.
+        // x of a full step goes global -> LDS directly (no registers, no
+        // LDS store instructions): direct load j of producer wave pw fills
+        // tile rows pw*64 + 8j .. +8 whole, lane i landing at LDS row i/8,
+        // physical chunk i%8, so the lane loads the logical chunk that the
+        // row's swizzle places there.
+        typedef __attribute__((address_space(3))) char lds_char;
+        const int pw = wave - kConsumers;
+        uint32_t xdoff[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = pw * 64 + 8 * j + (lane >> 3);
+            xdoff[j] = (uint32_t)min(r, m - 1 - m0) * (uint32_t)n_in * 2u + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+        }
+        auto load_x = [&](uint32_t buf, int kt) {
+            lds_char *dst = (lds_char *)smem + buf + pw * 64 * 128;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(dst + j * 8 * 128),
+                                                         16, xdoff[j], kt * (BK * 2), 0, 0);
+        };
+        // LDS byte offsets within a stage: x chunk i of this lane (32-wide
+        // tail step only), weight chunk j of slice i.  Rows of chunk (slice)
+        // i differ by multiples of 16 from those of chunk (slice) 0, so they
+        // share its swizzle.
         const int a_row = ptid >> 3, b_row = ptid / SPR, b_part = ptid % SPR;
         const uint32_t a_st = a_row * 128 + (((ptid & 7) ^ swz(a_row)) * 16);
         uint32_t b_st[CHS];
@@ -261,15 +310,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         // or packing of the loaded halves waits on loads of the same step.
         using SzBits = std::conditional_t<PAIR_SZ, uint16_t, uint32_t>;
         struct Regs {
-            u32x4 a[A_CHUNKS];
             u32x4 w[B_SLICES];
             SzBits s[B_SLICES], z[B_SLICES];            // raw fp16 bits (PAIR_SZ: z unused)
         };
-        // Global loads of step kt (kt < ksteps).
-        auto load_all = [&](Regs &g, int kt) {
-#pragma unroll
-            for (int i = 0; i < A_CHUNKS; ++i)
-                g.a[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * (BK * 2), 0);
+        constexpr int W_LOADS = B_SLICES * (PAIR_SZ ? 2 : 3);   // vector-memory ops of one load_w
+        // Weight loads of step kt (kt < ksteps).
+        auto load_w = [&](Regs &g, int kt) {
             const int gk = ((kt * BK) >> group_shift) * 2;
 #pragma unroll
             for (int i = 0; i < B_SLICES; ++i) {
@@ -316,10 +362,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
                 }
             }
         };
-        auto store_all = [&](const Regs &g, uint32_t buf) {
-#pragma unroll
-            for (int i = 0; i < A_CHUNKS; ++i)
-                *reinterpret_cast<u32x4 *>(smem + buf + a_st + i * PT * 16) = g.a[i];
+        auto store_w = [&](const Regs &g, uint32_t buf) {
 #pragma unroll
             for (int i = 0; i < B_SLICES; ++i) {
                 f16x2 scale, bias;
@@ -330,24 +373,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         if (ksteps > 0) {
             Regs R[3];
             const int kmax = ksteps - 1;
+            load_x(0, 0);
+            load_x(STAGE, min(1, kmax));
             // The prologue issues its loads in the loop's own order, pinned
             // by scheduling barriers, so the wait counts the compiler places
             // in the loop stay three steps deep.
-            load_all(R[0], 0);
+            load_w(R[0], 0);
             __builtin_amdgcn_sched_barrier(0);
-            load_all(R[1], min(1, kmax));
+            load_w(R[1], min(1, kmax));
             __builtin_amdgcn_sched_barrier(0);
-            load_all(R[2], min(2, kmax));
+            load_w(R[2], min(2, kmax));
             __builtin_amdgcn_sched_barrier(0);
-            store_all(R[0], 0);
+            store_w(R[0], 0);
             __builtin_amdgcn_sched_barrier(0);
-            load_all(R[0], min(3, kmax));
+            load_w(R[0], min(3, kmax));
             __builtin_amdgcn_sched_barrier(0);
-            store_all(R[1], STAGE);
+            store_w(R[1], STAGE);
             __builtin_amdgcn_sched_barrier(0);
-            load_all(R[1], min(4, kmax));
+            load_w(R[1], min(4, kmax));
             __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
+            wait_vmem<2 * W_LOADS>();
+            barrier_keep_vmem();
             // Step k with k % 3 == J: step k+2's registers (set (J+2) % 3)
             // into stage (J+2) % 3, which the consumers finished reading
             // before the previous barrier, then that set reloaded with step
@@ -356,11 +402,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
                 constexpr int J = decltype(J_)::value;
                 constexpr uint32_t wr = ((J + 2) % 3) * STAGE;
                 Regs &g = R[(J + 2) % 3];
-                store_all(g, wr);
+                load_x(wr, min(k + 2, kmax));
                 __builtin_amdgcn_sched_barrier(0);
-                load_all(g, min(k + 5, kmax));
+                store_w(g, wr);
                 __builtin_amdgcn_sched_barrier(0);
-                __syncthreads();
+                load_w(g, min(k + 5, kmax));
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmem<W_LOADS>();                   // this step's x (and every older load) landed
+                barrier_keep_vmem();
             };
             using I0 = std::integral_constant<int, 0>;
             using I1 = std::integral_constant<int, 1>;
