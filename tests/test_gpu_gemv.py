@@ -130,6 +130,32 @@ def test_gemv_llama70b_m8_sampled_rows(orc):
         assert_within_tolerance(y_rows, y_ref, a_ref, f"70B {lin.name} m=8")
 
 
+@pytest.mark.parametrize("m,n_out,n_in,g", [
+    (1, 12301, 8320, 128),     # rows of 8192+ codes, 769 tiles: two tiles per workgroup
+    (1, 8200, 16512, 128),     # long rows, 513 tiles: one tile per workgroup
+    (1, 8200, 16416, 32),      # the same without the scale fold; a partial last block
+    (3, 10250, 4224, 128),     # m > 1, 641 tiles: four tiles per workgroup
+])
+def test_gemv_paired_loads_ragged(orc, m, n_out, n_in, g):
+    """The dispatch rules that read weights as whole 128-byte lines of 8 rows,
+    on shapes with a partial last tile (n_out % 16 != 0) and an odd number of
+    128-wide blocks (the last pair's second block lies past the end) or a
+    partial last block; 384 sampled output channels and the last 20 against
+    the oracle."""
+    dev = torch.device("cuda:0")
+    w_dev = synthetic.normal_weight_device(n_out, n_in, n_out + n_in, 0.02, 2, dev)
+    x = synthetic.activations_f16(m, n_in, seed=n_in + m)
+    qw = w4.quantize_pack(w_dev, g)
+    y = w4.gemv(to_dev(x), qw)
+    rows = np.random.default_rng(n_out).choice(n_out, size=384, replace=False)
+    rows = np.unique(np.concatenate([rows, np.arange(n_out - 20, n_out)]))
+    w_rows = w_dev[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    del w_dev
+    packed, scales, zeros, _ = orc.quantize_pack(w_rows, g)
+    y_ref, a_ref = orc.linear_from_packed(x.view(np.uint16), packed, scales, zeros, g)
+    assert_within_tolerance(y[:, torch.from_numpy(rows).to(dev)], y_ref, a_ref, f"paired {m}x{n_out}x{n_in} g={g}")
+
+
 @pytest.fixture(scope="module")
 def stress_weights():
     """8192x28672 Student-t weights per group size (constant groups are placed

@@ -22,7 +22,9 @@
 // k = kb + 32q .. kb + 32q + 31.  MFMA number t (t = 0..3) takes from each of
 // the lane's words j the codes at nibble positions t and t + 4, i.e.
 // k = kb + 32q + 8j + {t, t+4}; x is stored in LDS in the same order, which
-// leaves every dot product unchanged.
+// leaves every dot product unchanged.  (On rows of 8192 codes and more the
+// weights of two blocks are read as whole 128-byte lines of 8 rows and
+// rearranged into this layout in registers; see PairAddr.)
 //
 // Two ways of forming B:
 //  * group_size 128 or 256 (every 128-wide k block lies in one group):
@@ -279,10 +281,71 @@ struct WeightAddr {
     }
 };
 
+// Paired weight loads (INT4).  HBM serves a load shaped 16 rows x 64 bytes
+// (one block of the fragment layout above) well below its streaming rate,
+// whole 128-byte lines far better.  So two loads cover a 16-row tile over
+// two blocks (256 codes, 128 bytes per row): load 0 reads rows 0-7, load 1
+// rows 8-15, each row as one whole 128-byte line.  Lane (column c, quarter
+// q) of load 0 reads row c % 8 at byte 16q (c < 8) or 64 + 16q (c >= 8);
+// load 1 reads row 8 + c % 8 at byte 64 + 16q (c < 8) or 16q (c >= 8).
+// A select gives each lane its own row's bytes 16q (first block), and the
+// other select, rotated by 8 lanes within the 16-lane row (DPP row_ror:8),
+// its bytes 64 + 16q (second block): exactly the fragment layout of the
+// two blocks.
+template <int CT>
+struct PairAddr {
+    const char *qbase;
+    const char *xsafe;            // 16-byte-aligned, L2-hot target for loads past the end
+    uint32_t rowoff[CT][2];       // byte offset of this lane's row, loads 0 and 1
+    uint32_t laneoff[2];          // byte offset within the 128-byte run
+    uint32_t last;                // last 16-byte slot of a row
+    int kblocks;
+
+    __device__ __forceinline__ void init(const uint32_t *qweight, const uint16_t *x, const Geometry &geo,
+                                         int row0, int col, int q)
+    {
+        const uint32_t row_bytes = (uint32_t)geo.words_per_row * 4u;
+        qbase = reinterpret_cast<const char *>(qweight) + (int64_t)row0 * row_bytes;
+        xsafe = reinterpret_cast<const char *>(x);
+        kblocks = geo.kblocks;
+        last = row_bytes - 16u;
+        const bool low = col < 8;
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            const int ra = min(t * 16 + (col & 7), geo.n_out - 1 - row0);
+            const int rb = min(t * 16 + 8 + (col & 7), geo.n_out - 1 - row0);
+            rowoff[t][0] = (uint32_t)ra * row_bytes;
+            rowoff[t][1] = (uint32_t)rb * row_bytes;
+        }
+        laneoff[0] = (low ? 0u : 64u) + 16u * (uint32_t)q;
+        laneoff[1] = (low ? 64u : 0u) + 16u * (uint32_t)q;
+    }
+    // Load h (0, 1) of pair p (blocks 2p, 2p+1) of tile t.  Bytes past the
+    // end of a row repeat its last 16 (they belong to padding quarters).
+    __device__ __forceinline__ u32x4 load(int p, int t, int h) const
+    {
+        const bool inside = 2 * p < kblocks;
+        const uint32_t off = inside ? rowoff[t][h] + min((uint32_t)p * 128u + laneoff[h], last) : 0u;
+        const char *base = inside ? qbase : xsafe;
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + off));
+    }
+};
+
+// The fragments of blocks 2p and 2p+1 from the two loads of a pair.
+__device__ __forceinline__ void unpair(const u32x4 &l0, const u32x4 &l1, bool low, u32x4 &b0, u32x4 &b1)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        b0[j] = low ? l0[j] : l1[j];
+        const uint32_t other = low ? l1[j] : l0[j];
+        b1[j] = (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0x128, 0xF, 0xF, false);   // row_ror:8
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Resident kernel: x and all scale|zero pairs staged once in LDS.
 // ---------------------------------------------------------------------------
-template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4>
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4, bool PAIRED = false>
 __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -308,16 +371,30 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     const int row0 = blockIdx.x * ROWS;
 
     constexpr int LPB = BITS / 4;                  // 16-byte weight loads per block per tile
+    static_assert(!PAIRED || (BITS == 4 && UNROLL % 2 == 0), "paired loads cover two INT4 blocks");
     WeightAddr<CT, BITS> wa;
     wa.init(qweight, x, geo, row0, col, quarter);
+    PairAddr<CT> pa;
+    if constexpr (PAIRED) pa.init(qweight, x, geo, row0, col, quarter);
     auto load_stage = [&](Stage<CT, UNROLL, BITS> &st, int i) {
+        if constexpr (PAIRED) {
+            // slots 2v, 2v+1 hold the two loads of pair (i * SPLIT + wave) * UNROLL / 2 + v
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+            for (int v = 0; v < UNROLL / 2; ++v)
 #pragma unroll
-            for (int t = 0; t < CT; ++t)
+                for (int t = 0; t < CT; ++t)
 #pragma unroll
-                for (int l = 0; l < LPB; ++l)
-                    st.w[u][t * LPB + l] = wa.load((i * SPLIT + wave) * UNROLL + u, t, l);
+                    for (int h = 0; h < 2; ++h)
+                        st.w[2 * v + h][t] = pa.load((i * SPLIT + wave) * (UNROLL / 2) + v, t, h);
+        } else {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+#pragma unroll
+                    for (int l = 0; l < LPB; ++l)
+                        st.w[u][t * LPB + l] = wa.load((i * SPLIT + wave) * UNROLL + u, t, l);
+        }
     };
 
     // ---- staging of x (chunk c = (row, block, quarter) holds 32 values) and
@@ -404,6 +481,15 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     const char *xrow = x_lds + min(col, m - 1) * geo.x_row_bytes;
     const uint32_t *szrow = sz_lds + col * geo.sz_stride;
     auto compute = [&](const Stage<CT, UNROLL, BITS> &st, int i) {
+        Stage<CT, UNROLL, BITS> up;                // PAIRED: the loads turned into block fragments
+        if constexpr (PAIRED) {
+#pragma unroll
+            for (int v = 0; v < UNROLL / 2; ++v)
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+                    unpair(st.w[2 * v][t], st.w[2 * v + 1][t], col < 8, up.w[2 * v][t], up.w[2 * v + 1][t]);
+        }
+        const Stage<CT, UNROLL, BITS> &frag = PAIRED ? up : st;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = (i * SPLIT + wave) * UNROLL + u;
@@ -419,7 +505,7 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
             uint32_t sz[CT];
 #pragma unroll
             for (int t = 0; t < CT; ++t) sz[t] = szrow[t * 16 * geo.sz_stride + g];
-            process_block<CT, FOLD, BITS>(acc, a, st.w[u], sz, wa.valid(kb));
+            process_block<CT, FOLD, BITS>(acc, a, frag.w[u], sz, wa.valid(kb));
         }
     };
 
@@ -614,7 +700,7 @@ hipError_t allow_full_lds(K kernel)
     return e;
 }
 
-template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4>
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4, bool PAIRED = false>
 bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                    const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
                    uint16_t *y, hipStream_t stream, hipError_t *err)
@@ -629,7 +715,7 @@ bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *s
     const size_t part = SPLIT > 1 ? (size_t)SPLIT * CT * 1024 : 0;
     const size_t lds = (x_bytes > part ? x_bytes : part) + (size_t)16 * CT * g.sz_stride * 4;
     if (lds > kMaxLds) return false;
-    auto kernel = gemv_resident_kernel<SPLIT, CT, UNROLL, DEPTH, FOLD, BITS>;
+    auto kernel = gemv_resident_kernel<SPLIT, CT, UNROLL, DEPTH, FOLD, BITS, PAIRED>;
     if (lds > 64 * 1024) {
         const hipError_t e = allow_full_lds(kernel);
         if (e != hipSuccess) {
@@ -677,7 +763,11 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 
 // Configurations chosen from measured sweeps on MI355X over the decode
 // shapes (7B and 70B projections, m = 1 and 8, INT4 and INT8); other shapes
-// fall through to the nearest rule.  Every rule ends in a configuration that always fits.
+// fall through to the nearest rule.  Paired loads pay on rows of 8192 codes
+// and more (9-26 % on the 70B and 8192x28672 shapes); on the 4096-wide 7B
+// linears, whose launches are short and dependent, they measured the same
+// as the fragment-order loads, which are kept there.  Every rule ends in a
+// configuration that always fits.
 template <bool FOLD, int BITS>
 hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
@@ -688,6 +778,8 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
     const int tiles = (n_out + 15) / 16;
 #define Q4_RES(S, C, U, D) \
     if (plan_resident<S, C, U, D, FOLD, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+#define Q4_PAIR(S, C, U, D) \
+    if (plan_resident<S, C, U, D, FOLD, BITS, BITS == 4>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
 #define Q4_WIN(S, C, U, MM) \
     if (plan_window<S, C, U, FOLD, MM, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
     if (kblocks >= 16) {
@@ -704,18 +796,19 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
         } else if (!FOLD) {
             if (m == 1) {
                 if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 1, 3);
-                if (kblocks >= 128 && tiles >= 512) Q4_RES(16, 1, 1, 2);
+                if (kblocks >= 128 && tiles >= 512) Q4_PAIR(16, 1, 2, 1);
                 if (tiles <= 768) Q4_RES(8, 1, 1, 2);
                 Q4_RES(4, 2, 1, 2);
             }
             Q4_RES(16, 1, 1, 4);
         } else if (m == 1) {
             if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 1, 3);
-            if (kblocks >= 128 && tiles >= 512) Q4_RES(8, 2, 1, 2);
+            if (kblocks >= 128 && tiles >= 512) Q4_PAIR(8, 1, 2, 2);
             if (tiles <= 768) Q4_RES(8, 1, 1, 2);
+            if (kblocks >= 64) Q4_PAIR(4, 2, 2, 2);
             Q4_RES(4, 2, 1, 2);
         } else {
-            if (tiles >= 640) Q4_RES(8, 4, 1, 2);
+            if (tiles >= 640) Q4_PAIR(8, 4, 2, 1);
             if (tiles >= 256) Q4_RES(8, 2, 1, 2);
             Q4_RES(8, 1, 1, 2);
         }
@@ -725,6 +818,7 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
     Q4_RES(4, 1, 1, 2);
     Q4_WIN(2, 1, 1, 16);
 #undef Q4_RES
+#undef Q4_PAIR
 #undef Q4_WIN
     return hipErrorInvalidValue;                // unreachable: the last window always fits
 }
