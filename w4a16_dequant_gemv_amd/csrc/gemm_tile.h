@@ -1,6 +1,7 @@
 // gemm_tile.h -- device helpers shared by the LDS-staged MFMA GEMM kernels
 // (W4A16 / W8A16 in q4_gemm.hip, W8A8 in w8a8.hip): the XCD-aware tile order,
-// the LDS chunk swizzle, buffer-resource flags and scheduling-group patterns.
+// the LDS chunk swizzle, buffer-resource flags, scheduling-group patterns and
+// the waits that let direct global->LDS loads stay in flight across barriers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,3 +60,26 @@ __device__ __forceinline__ void interleave()
     }
 }
 
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt 7 and
+// lgkmcnt 15 mean no wait on those); the empty asm statements keep the
+// compiler from moving memory accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem()
+{
+    static_assert(N >= 0 && N < 64, "the vector-memory counter has six bits");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only
+// (lgkmcnt 0), leaving its vector-memory loads, direct LDS loads included,
+// in flight; __syncthreads() would wait for all of them.
+__device__ __forceinline__ void barrier_keep_vmem()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}

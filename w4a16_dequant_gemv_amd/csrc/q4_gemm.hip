@@ -93,28 +93,6 @@ __device__ __forceinline__ u32x2 dequant_byte_word(uint32_t w, f16x2 bias, f16x2
 constexpr int kConsumers = 4, kProducers = 4;
 constexpr int kGemmThreads = 64 * (kConsumers + kProducers);
 
-// Wait until at most N vector-memory operations of this wave are
-// outstanding; the empty asm statements keep the compiler from moving
-// memory accesses across the wait.
-template <int N>
-__device__ __forceinline__ void wait_vmem()
-{
-    static_assert(N >= 0 && N < 64, "the vector-memory counter has six bits");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-    asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier that waits for this wave's LDS operations only, leaving
-// its vector-memory loads in flight.
-__device__ __forceinline__ void barrier_keep_vmem()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // PAIR_SZ: the two lanes of each lane pair dequantize slices of the same
 // row and group (every case but INT4 with groups of 32), so the even lane
 // loads the scale, the odd lane the zero-point, and a DPP swap gives each
@@ -289,11 +267,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
             xdoff[j] = (uint32_t)min(r, m - 1 - m0) * (uint32_t)n_in * 2u + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
         }
         auto load_x = [&](uint32_t buf, int kt) {
+            // (the offsets are passed as int explicitly: with an implicit
+            // conversion this toolchain's host pass dropped the kernel's launch stub)
             lds_char *dst = (lds_char *)smem + buf + pw * 64 * 128;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(dst + j * 8 * 128),
-                                                         16, xdoff[j], kt * (BK * 2), 0, 0);
+                                                         16, (int)xdoff[j], kt * (BK * 2), 0, 0);
         };
         // LDS byte offsets within a stage: x chunk i of this lane (32-wide
         // tail step only), weight chunk j of slice i.  Rows of chunk (slice)
