@@ -131,3 +131,31 @@ def test_int8_rejects_bad_group(orc):
     w = torch.zeros((8, 96), dtype=torch.float32, device="cuda")
     with pytest.raises(w4.W4A16Error):
         w4.quantize_pack(w, 48, bits=8)
+
+
+@pytest.mark.parametrize("m,n_out,n_in,g", [
+    (1, 12301, 4160, None),    # 769 tiles, per-channel, a partial last 128-wide block
+    (1, 8200, 16416, None),    # long rows, 513 tiles, a partial last block
+    (8, 10250, 4224, 128),     # m > 4, 641 tiles: four tiles per workgroup
+    (8, 700, 2080, 32),        # m > 4, two tiles per workgroup, a partial last block
+    (1, 130, 2080, 32),        # few tiles, a partial last block
+])
+def test_int8_paired_loads_ragged(orc, m, n_out, n_in, g):
+    """INT8 GEMV shapes on the paired-load rules (two 16-byte halves of a
+    block read as whole 128-byte lines of 8 rows), with a partial last tile
+    (n_out % 16 != 0); 384 sampled output channels and the last 20 against
+    the oracle."""
+    gs = n_in if g is None else g
+    dev = torch.device("cuda:0")
+    w_dev = synthetic.normal_weight_device(n_out, n_in, n_out + 7 * n_in, 0.02, 2, dev)
+    x = synthetic.activations_f16(m, n_in, seed=n_in + 5 * m)
+    qw = w4.quantize_pack(w_dev, gs, bits=8)
+    y = w4.gemv(to_dev(x), qw)
+    rows = np.random.default_rng(n_out + 1).choice(n_out, size=min(384, n_out), replace=False)
+    rows = np.unique(np.concatenate([rows, np.arange(n_out - 20, n_out)]))
+    w_rows = w_dev[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    del w_dev
+    packed, scales, zeros, _ = orc.quantize_pack(w_rows, gs, False, bits=8)
+    y_ref, a_ref = orc.linear_from_packed(x.view(np.uint16), packed, scales, zeros, gs, bits=8)
+    assert_within_tolerance(y[:, torch.from_numpy(rows).to(dev)], y_ref, a_ref,
+                            f"q8 paired {m}x{n_out}x{n_in} g={gs}")

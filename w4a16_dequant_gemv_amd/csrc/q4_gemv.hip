@@ -281,18 +281,18 @@ struct WeightAddr {
     }
 };
 
-// Paired weight loads (INT4).  HBM serves a load shaped 16 rows x 64 bytes
-// (one block of the fragment layout above) well below its streaming rate,
-// whole 128-byte lines far better.  So two loads cover a 16-row tile over
-// two blocks (256 codes, 128 bytes per row): load 0 reads rows 0-7, load 1
-// rows 8-15, each row as one whole 128-byte line.  Lane (column c, quarter
-// q) of load 0 reads row c % 8 at byte 16q (c < 8) or 64 + 16q (c >= 8);
-// load 1 reads row 8 + c % 8 at byte 64 + 16q (c < 8) or 16q (c >= 8).
-// A select gives each lane its own row's bytes 16q (first block), and the
-// other select, rotated by 8 lanes within the 16-lane row (DPP row_ror:8),
-// its bytes 64 + 16q (second block): exactly the fragment layout of the
-// two blocks.
-template <int CT>
+// Paired weight loads.  HBM serves a load shaped 16 rows x 64 bytes (the
+// fragment layout above) well below its streaming rate, whole 128-byte lines
+// far better.  So two loads cover a 16-row tile over 128 bytes per row (two
+// INT4 blocks, or one INT8 block): load 0 reads rows 0-7, load 1 rows 8-15,
+// each row as one whole 128-byte line, and a select plus a rotation by 8
+// lanes within each 16-lane row (DPP row_ror:8) turn them into the
+// fragments.  INT4: lane (column c, quarter q) of load 0 reads row c % 8 at
+// byte 16q (c < 8) or 64 + 16q (c >= 8), load 1 row 8 + c % 8 the other way
+// round, so the select gives each lane its row's bytes 16q (first block) and
+// the rotated other select its bytes 64 + 16q (second block).  INT8: the
+// same with bytes 32q and 32q + 16, the two 16-byte halves of one block.
+template <int CT, int BITS>
 struct PairAddr {
     const char *qbase;
     const char *xsafe;            // 16-byte-aligned, L2-hot target for loads past the end
@@ -317,21 +317,25 @@ struct PairAddr {
             rowoff[t][0] = (uint32_t)ra * row_bytes;
             rowoff[t][1] = (uint32_t)rb * row_bytes;
         }
-        laneoff[0] = (low ? 0u : 64u) + 16u * (uint32_t)q;
-        laneoff[1] = (low ? 64u : 0u) + 16u * (uint32_t)q;
+        const uint32_t first = BITS == 4 ? 16u * (uint32_t)q : 32u * (uint32_t)q;
+        const uint32_t second = BITS == 4 ? 64u + 16u * (uint32_t)q : 32u * (uint32_t)q + 16u;
+        laneoff[0] = low ? first : second;
+        laneoff[1] = low ? second : first;
     }
-    // Load h (0, 1) of pair p (blocks 2p, 2p+1) of tile t.  Bytes past the
-    // end of a row repeat its last 16 (they belong to padding quarters).
+    // Load h (0, 1) of run p (128 bytes per row: INT4 blocks 2p and 2p+1,
+    // INT8 block p) of tile t.  Bytes past the end of a row repeat its last
+    // 16 (they belong to padding quarters).
     __device__ __forceinline__ u32x4 load(int p, int t, int h) const
     {
-        const bool inside = 2 * p < kblocks;
+        const bool inside = (BITS == 4 ? 2 * p : p) < kblocks;
         const uint32_t off = inside ? rowoff[t][h] + min((uint32_t)p * 128u + laneoff[h], last) : 0u;
         const char *base = inside ? qbase : xsafe;
         return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + off));
     }
 };
 
-// The fragments of blocks 2p and 2p+1 from the two loads of a pair.
+// The fragments (INT4: of blocks 2p and 2p+1; INT8: the two halves of block
+// p) from the two loads of a pair.
 __device__ __forceinline__ void unpair(const u32x4 &l0, const u32x4 &l1, bool low, u32x4 &b0, u32x4 &b1)
 {
 #pragma unroll
@@ -371,13 +375,13 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     const int row0 = blockIdx.x * ROWS;
 
     constexpr int LPB = BITS / 4;                  // 16-byte weight loads per block per tile
-    static_assert(!PAIRED || (BITS == 4 && UNROLL % 2 == 0), "paired loads cover two INT4 blocks");
+    static_assert(!PAIRED || BITS == 8 || UNROLL % 2 == 0, "paired INT4 loads cover two blocks");
     WeightAddr<CT, BITS> wa;
     wa.init(qweight, x, geo, row0, col, quarter);
-    PairAddr<CT> pa;
+    PairAddr<CT, BITS> pa;
     if constexpr (PAIRED) pa.init(qweight, x, geo, row0, col, quarter);
     auto load_stage = [&](Stage<CT, UNROLL, BITS> &st, int i) {
-        if constexpr (PAIRED) {
+        if constexpr (PAIRED && BITS == 4) {
             // slots 2v, 2v+1 hold the two loads of pair (i * SPLIT + wave) * UNROLL / 2 + v
 #pragma unroll
             for (int v = 0; v < UNROLL / 2; ++v)
@@ -386,6 +390,14 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
                         st.w[2 * v + h][t] = pa.load((i * SPLIT + wave) * (UNROLL / 2) + v, t, h);
+        } else if constexpr (PAIRED) {
+            // INT8: the two loads of a block sit where its two halves go
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) st.w[u][t * 2 + h] = pa.load((i * SPLIT + wave) * UNROLL + u, t, h);
         } else {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u)
@@ -482,12 +494,18 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
     const uint32_t *szrow = sz_lds + col * geo.sz_stride;
     auto compute = [&](const Stage<CT, UNROLL, BITS> &st, int i) {
         Stage<CT, UNROLL, BITS> up;                // PAIRED: the loads turned into block fragments
-        if constexpr (PAIRED) {
+        if constexpr (PAIRED && BITS == 4) {
 #pragma unroll
             for (int v = 0; v < UNROLL / 2; ++v)
 #pragma unroll
                 for (int t = 0; t < CT; ++t)
                     unpair(st.w[2 * v][t], st.w[2 * v + 1][t], col < 8, up.w[2 * v][t], up.w[2 * v + 1][t]);
+        } else if constexpr (PAIRED) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+                    unpair(st.w[u][t * 2], st.w[u][t * 2 + 1], col < 8, up.w[u][t * 2], up.w[u][t * 2 + 1]);
         }
         const Stage<CT, UNROLL, BITS> &frag = PAIRED ? up : st;
 #pragma unroll
@@ -763,11 +781,13 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 
 // Configurations chosen from measured sweeps on MI355X over the decode
 // shapes (7B and 70B projections, m = 1 and 8, INT4 and INT8); other shapes
-// fall through to the nearest rule.  Paired loads pay on rows of 8192 codes
-// and more (9-26 % on the 70B and 8192x28672 shapes); on the 4096-wide 7B
-// linears, whose launches are short and dependent, they measured the same
-// as the fragment-order loads, which are kept there.  Every rule ends in a
-// configuration that always fits.
+// fall through to the nearest rule.  Paired INT4 loads pay on rows of 8192
+// codes and more (9-26 % on the 70B and 8192x28672 shapes); on the
+// 4096-wide 7B linears, whose launches are short and dependent, they
+// measured the same as the fragment-order loads, which are kept there.
+// INT8 rows are twice as long in bytes and paired loads pay on every
+// measured shape (3-36 %).  Every rule ends in a configuration that always
+// fits.
 template <bool FOLD, int BITS>
 hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
@@ -779,20 +799,23 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
 #define Q4_RES(S, C, U, D) \
     if (plan_resident<S, C, U, D, FOLD, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
 #define Q4_PAIR(S, C, U, D) \
-    if (plan_resident<S, C, U, D, FOLD, BITS, BITS == 4>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+    if (plan_resident<S, C, U, D, FOLD, BITS, true>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
 #define Q4_WIN(S, C, U, MM) \
     if (plan_window<S, C, U, FOLD, MM, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
     if (kblocks >= 16) {
         if constexpr (BITS == 8) {
             // twice the bytes per code: fewer waves per tile keep more
-            // workgroups in flight per CU
+            // workgroups in flight per CU; paired loads throughout
             if (m == 1) {
-                if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 2, 2);
-                if (tiles <= 256) Q4_RES(4, 1, 1, 3);
-                Q4_RES(4, 1, 1, 2);
+                if (tiles <= 256 && kblocks >= 64) Q4_PAIR(8, 1, 1, 3);
+                if (tiles <= 256) Q4_PAIR(8, 1, 1, 2);
+                if (kblocks >= 128) Q4_PAIR(8, 1, 1, 3);
+                if (tiles <= 768) Q4_PAIR(4, 1, 1, 2);
+                Q4_PAIR(4, 2, 1, 1);
             }
             if (m <= 4) Q4_RES(8, 1, 1, 2);
-            Q4_RES(8, 2, 1, 2);
+            if (tiles >= 640) Q4_PAIR(8, 4, 1, 1);
+            Q4_PAIR(8, 2, 1, 2);
         } else if (!FOLD) {
             if (m == 1) {
                 if (tiles <= 256 && kblocks >= 64) Q4_RES(8, 1, 1, 3);
