@@ -226,6 +226,41 @@ __global__ __launch_bounds__(256) void dequant_kernel(
         dst[j] = make_float4(r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]);
 }
 
+// INT4 dequantization: one lane per 16-bit half word (four codes) and one
+// float4 of output, ITEMS runs of 256 lanes per workgroup, so every store
+// instruction of a wave writes 1 KiB of contiguous output (one lane per
+// packed word would split each 32-byte output span over two half-covered
+// store instructions, which HBM serves markedly slower).
+// The group of half word f is f >> shift, or its row (f / per_row) for
+// per-channel weights.
+template <int ITEMS, bool PER_CHANNEL>
+__global__ __launch_bounds__(256) void dequant4_kernel(
+    const uint16_t *__restrict__ q16, const uint16_t *__restrict__ scales,
+    const uint16_t *__restrict__ zeros, float *__restrict__ out, int64_t n4, int group_shift4, int64_t per_row)
+{
+    const int64_t base = (int64_t)blockIdx.x * (256 * ITEMS) + threadIdx.x;
+    uint32_t q[ITEMS];
+    int64_t grp[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int64_t f = base + (int64_t)it * 256;
+        const int64_t fc = f < n4 ? f : n4 - 1;
+        q[it] = q16[fc];
+        grp[it] = PER_CHANNEL ? fc / per_row : fc >> group_shift4;
+    }
+    float4 *dst = reinterpret_cast<float4 *>(out);
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int64_t f = base + (int64_t)it * 256;
+        const float sc = half_bits_to_float(scales[grp[it]]);
+        const int z = (int)half_bits_to_float(zeros[grp[it]]);
+        float r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = sc * (float)((int)((q[it] >> (4 * i)) & 15u) - z);
+        if (f < n4) dst[f] = make_float4(r[0], r[1], r[2], r[3]);
+    }
+}
+
 template <bool SYMMETRIC, int BITS>
 hipError_t launch_quantize(const float *w, int64_t n_out, int64_t n_in, int group_size,
                            uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
@@ -266,6 +301,21 @@ hipError_t launch_dequant(const uint32_t *qweight, const uint16_t *scales, const
     constexpr int PER_WORD = Codes<BITS>::PER_WORD;
     const int64_t words_per_row = n_in / PER_WORD;
     const int64_t n_words = n_out * words_per_row;
+    if constexpr (BITS == 4) {
+        constexpr int ITEMS = 4;
+        const int64_t n4 = n_words * 2;
+        const dim3 grid4((unsigned)((n4 + 256 * ITEMS - 1) / (256 * ITEMS))), block4(256);
+        const uint16_t *q16 = reinterpret_cast<const uint16_t *>(qweight);
+        const int per_group = group_size / 4;
+        if ((per_group & (per_group - 1)) == 0) {
+            int shift = 0;
+            while ((1 << shift) < per_group) ++shift;
+            dequant4_kernel<ITEMS, false><<<grid4, block4, 0, stream>>>(q16, scales, zeros, out, n4, shift, n_in / 4);
+        } else {                                        // per-channel with a row of other length
+            dequant4_kernel<ITEMS, true><<<grid4, block4, 0, stream>>>(q16, scales, zeros, out, n4, 0, n_in / 4);
+        }
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((n_words + 255) / 256)), block(256);
     const int words_per_group = group_size / PER_WORD;
     if ((words_per_group & (words_per_group - 1)) == 0) {
