@@ -23,7 +23,8 @@ MUTANTS = {
     "sym_divisor_2b_minus_1": ("const float qmax = (float)((1 << (bits - 1)) - 1);",
                                "const float qmax = (float)((1 << bits) - 1);"),
     "sym_offset_7": ("codes[t] + offset : codes[t]", "codes[t] + offset - 1 : codes[t]"),
-    "sym_offset_fixed_8": ("const int32_t offset = 1 << (bits - 1);", "const int32_t offset = 8;"),
+    "sym_offset_fixed_8": ("const int64_t groups = n_in / group_size;\n    const int32_t offset = 1 << (bits - 1);",
+                           "const int64_t groups = n_in / group_size;\n    const int32_t offset = 8;"),
     "nibble_order_reversed": ("row[k / per_word] |= u << (bits * (k % per_word));",
                               "row[k / per_word] |= u << (bits * (per_word - 1 - k % per_word));"),
     "pack_shift_4": ("row[k / per_word] |= u << (bits * (k % per_word));",
