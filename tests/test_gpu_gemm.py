@@ -77,3 +77,39 @@ def test_gemm_prefill_2048_sampled_rows(orc, idx):
     y_ref, a_ref = orc.linear_from_packed(x[rows].view(np.uint16), packed, scales, zeros, 128)
     assert_within_tolerance(y[torch.from_numpy(rows).to(y.device)], y_ref, a_ref,
                             f"prefill {lin.n_out}x{lin.n_in}")
+
+
+def _with_meta_offset(qw, offset):
+    """The same weights with scales and zeros copied `offset` halves into
+    fresh buffers (offset 1: only 2-byte aligned, 2: 4-byte aligned)."""
+    from w4a16_dequant_gemv_amd.api import QuantizedWeight
+
+    def moved(t):
+        buf = torch.zeros(t.numel() + 8, dtype=t.dtype, device=t.device)
+        view = buf[offset:offset + t.numel()].view(t.shape)
+        view.copy_(t)
+        return view
+    return QuantizedWeight(qw.qweight, moved(qw.scales), moved(qw.zeros), qw.n_out, qw.n_in, qw.group_size,
+                           qw.symmetric, qw.bits)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("n_out,n_in,g", [(96, 1024, 64), (80, 2048, 256), (72, 4608, 256), (64, 640, 64),
+                                          (130, 4096, 128), (40, 2816, 128), (33, 1088, 64)])
+def test_gemm_scale_runs(orc, bits, n_out, n_in, g):
+    """Groups of 64..256: the producers read runs of 8 (16-byte aligned
+    metadata, groups per row a multiple of 8) or 2 (4-byte aligned, even)
+    groups' scales and zero-points at once, else one per step.  Every form
+    gives the same bits, within tolerance of the oracle."""
+    w = synthetic.normal_weight(n_out, n_in, seed=7 * n_out + n_in, std=0.02,
+                                n_outlier_cols=synthetic.n_outliers(n_in))
+    x = synthetic.activations_f16(300, n_in, seed=11 + n_in)
+    packed, scales, zeros, _ = orc.quantize_pack(w, g, bits=bits)
+    qw = qweight_from_oracle(packed, scales, zeros, g, bits=bits)
+    xd = to_dev(x)
+    ys = [w4.gemm(xd, _with_meta_offset(qw, off)) for off in (0, 1, 2)]
+    torch.cuda.synchronize()
+    y_ref, a_ref = orc.linear_from_packed(x.view(np.uint16), packed, scales, zeros, g, bits=bits)
+    assert_within_tolerance(ys[0], y_ref, a_ref, f"q{bits} gemm {n_out}x{n_in} g={g}")
+    for off, y in zip((1, 2), ys[1:]):
+        assert_bits_equal(f16_bits(y), f16_bits(ys[0]), f"q{bits} gemm {n_out}x{n_in} g={g} metadata offset {off}")

@@ -99,13 +99,19 @@ constexpr int kGemmThreads = 64 * (kConsumers + kProducers);
 // row and group (every case but INT4 with groups of 32), so the even lane
 // loads the scale, the odd lane the zero-point, and a DPP swap gives each
 // lane both: one 2-byte gather per slice and step instead of two.
-template <int BM, int BN, int BITS, bool PAIR_SZ>
+// SZV > 1 (with PAIR_SZ, groups of 64..256): the lane loads the raw bits of
+// SZV consecutive groups of its row at once, every sz_log2p-th power of two
+// steps, and keeps them in registers.  The per-step 2-byte gathers, each
+// touching a line per row, were a sixth of the workgroup's L2 requests and
+// cost about 15 % of the step time.
+template <int BM, int BN, int BITS, bool PAIR_SZ, int SZV = 1>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     uint16_t *__restrict__ y, int m, int n_out, int n_in, int group_shift,
-    int tiles_m, int tiles_n)
+    int tiles_m, int tiles_n, int sz_log2p)
 {
+    static_assert(SZV == 1 || (PAIR_SZ && (SZV == 2 || SZV == 8)), "scale vectors of 2 or 8 groups");
     constexpr int BK = 64;
     constexpr int PT = 64 * kProducers;                 // producer threads
     constexpr int WT_M = BM / kConsumers, WT_N = BN;    // consumer wave tile
@@ -281,32 +287,62 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         // Register type of the raw scale/zero bits, chosen so that no masking
         // or packing of the loaded halves waits on loads of the same step.
         using SzBits = std::conditional_t<PAIR_SZ, uint16_t, uint32_t>;
+        using SzVec = std::conditional_t<SZV == 8, u32x4, uint32_t>;   // SZV raw halves
         struct Regs {
             u32x4 w[B_SLICES];
-            SzBits s[B_SLICES], z[B_SLICES];            // raw fp16 bits (PAIR_SZ: z unused)
+            SzBits s[B_SLICES], z[B_SLICES];            // raw fp16 bits (PAIR_SZ: z unused; SZV > 1: unused)
+            SzVec v[B_SLICES];                          // SZV > 1: the groups from step kt on, if loaded
         };
-        constexpr int W_LOADS = B_SLICES * (PAIR_SZ ? 2 : 3);   // vector-memory ops of one load_w
+        constexpr int W_LOADS = B_SLICES * (SZV > 1 ? 1 : PAIR_SZ ? 2 : 3);   // per load_w (SZV > 1: without the vector)
+        // SZV > 1: data step kt loads a new vector when kt is a multiple of
+        // 2^sz_log2p (a new run of SZV groups begins there).
+        const int sz_mask = (1 << sz_log2p) - 1;
+        auto sz_due = [&](int kt) { return SZV > 1 && (kt & sz_mask) == 0; };
         // Weight loads of step kt (kt < ksteps).
         auto load_w = [&](Regs &g, int kt) {
             const int gk = ((kt * BK) >> group_shift) * 2;
 #pragma unroll
             for (int i = 0; i < B_SLICES; ++i) {
                 g.w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * (BK * BITS / 8), 0);
-                if constexpr (PAIR_SZ) {
+                if constexpr (SZV > 1) {
+                    (void)gk;
+                } else if constexpr (PAIR_SZ) {
                     g.s[i] = szp[i][gk >> 1];
                 } else {
                     g.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff[i], gk, 0);
                     g.z[i] = __builtin_amdgcn_raw_buffer_load_b16(zr, soff[i], gk, 0);
                 }
             }
+            if constexpr (SZV > 1) {
+                if (sz_due(kt)) {
+                    const int first = (kt >> sz_log2p) * SZV;           // first group of the run
+#pragma unroll
+                    for (int i = 0; i < B_SLICES; ++i) g.v[i] = *reinterpret_cast<const SzVec *>(szp[i] + first);
+                }
+            }
+        };
+        // SZV > 1: the run of groups that the steps being stored use, and
+        // this lane's raw scale (or zero-point) bits of slice i at step kt.
+        SzVec cur[B_SLICES];
+        auto sz_bits = [&](const Regs &g, int i, int kt) -> uint32_t {
+            if constexpr (SZV > 1) {
+                const int e = ((kt * BK) >> group_shift) & (SZV - 1);   // group within the run
+                uint32_t d;
+                if constexpr (SZV == 8) d = cur[i][e >> 1];
+                else d = cur[i];
+                return (d >> (16 * (e & 1))) & 0xFFFFu;
+            } else {
+                return g.s[i];
+            }
         };
         // Scale and biased zero-point (1024 + z) of slice i as fp16 pairs.
-        auto scale_bias = [&](const Regs &g, int i, f16x2 &scale, f16x2 &bias) {
+        auto scale_bias = [&](const Regs &g, int i, int kt, f16x2 &scale, f16x2 &bias) {
             uint32_t sb, zb;
             if constexpr (PAIR_SZ) {
-                const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)g.s[i], 0xB1, 0xF, 0xF, false);
-                sb = (tid & 1) ? other : g.s[i];
-                zb = (tid & 1) ? g.s[i] : other;
+                const uint32_t own = sz_bits(g, i, kt);
+                const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+                sb = (tid & 1) ? other : own;
+                zb = (tid & 1) ? own : other;
             } else {
                 sb = g.s[i];
                 zb = g.z[i];
@@ -334,14 +370,34 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
                 }
             }
         };
-        auto store_w = [&](const Regs &g, uint32_t buf) {
+        // Data step kt (stores go in increasing kt, so cur holds the run
+        // that the last due step loaded).
+        auto store_w = [&](const Regs &g, uint32_t buf, int kt) {
+            if constexpr (SZV > 1) {
+                if (sz_due(kt)) {
+#pragma unroll
+                    for (int i = 0; i < B_SLICES; ++i) cur[i] = g.v[i];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < B_SLICES; ++i) {
                 f16x2 scale, bias;
-                scale_bias(g, i, scale, bias);
+                scale_bias(g, i, kt, scale, bias);
                 store_slice(buf, i, g.w[i], scale, bias);
             }
         };
+        // Wait until at most n vector-memory operations remain, n being the
+        // loads of the last one or two load_w calls (their scale vectors
+        // included when due); the count is an immediate, so each possible n
+        // has its own wait.
+        auto wait_left = [&](int n) {
+            if (n == W_LOADS) wait_vmem<W_LOADS>();
+            else if (n == W_LOADS + B_SLICES) wait_vmem<W_LOADS + B_SLICES>();
+            else if (n == 2 * W_LOADS) wait_vmem<2 * W_LOADS>();
+            else if (n == 2 * W_LOADS + B_SLICES) wait_vmem<2 * W_LOADS + B_SLICES>();
+            else wait_vmem<2 * W_LOADS + 2 * B_SLICES>();
+        };
+        auto vec_loads = [&](int kt) { return sz_due(kt) ? B_SLICES : 0; };
         if (ksteps > 0) {
             Regs R[3];
             const int kmax = ksteps - 1;
@@ -356,15 +412,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
             __builtin_amdgcn_sched_barrier(0);
             load_w(R[2], min(2, kmax));
             __builtin_amdgcn_sched_barrier(0);
-            store_w(R[0], 0);
+            store_w(R[0], 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             load_w(R[0], min(3, kmax));
             __builtin_amdgcn_sched_barrier(0);
-            store_w(R[1], STAGE);
+            store_w(R[1], STAGE, min(1, kmax));
             __builtin_amdgcn_sched_barrier(0);
             load_w(R[1], min(4, kmax));
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmem<2 * W_LOADS>();
+            wait_left(2 * W_LOADS + vec_loads(min(3, kmax)) + vec_loads(min(4, kmax)));
             barrier_keep_vmem();
             // Step k with k % 3 == J: step k+2's registers (set (J+2) % 3)
             // into stage (J+2) % 3, which the consumers finished reading
@@ -376,11 +432,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
                 Regs &g = R[(J + 2) % 3];
                 load_x(wr, min(k + 2, kmax));
                 __builtin_amdgcn_sched_barrier(0);
-                store_w(g, wr);
+                store_w(g, wr, min(k + 2, kmax));
                 __builtin_amdgcn_sched_barrier(0);
                 load_w(g, min(k + 5, kmax));
                 __builtin_amdgcn_sched_barrier(0);
-                wait_vmem<W_LOADS>();                   // this step's x (and every older load) landed
+                wait_left(W_LOADS + vec_loads(min(k + 5, kmax)));   // this step's x (and every older load) landed
                 barrier_keep_vmem();
             };
             using I0 = std::integral_constant<int, 0>;
@@ -467,20 +523,41 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
 }
 
-template <int BM, int BN, int BITS, bool PAIR_SZ>
+template <int BM, int BN, int BITS, bool PAIR_SZ, int SZV = 1>
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                        const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
                        uint16_t *y, hipStream_t stream)
 {
     const int tiles_m = (m + BM - 1) / BM, tiles_n = (n_out + BN - 1) / BN;
     const size_t lds = kStages * (size_t)(BM + BN) * 128;
-    auto kernel = gemm_kernel<BM, BN, BITS, PAIR_SZ>;
+    // steps per run of SZV groups: SZV << (group_shift - 6), a power of two
+    int sz_log2p = 0;
+    if (SZV > 1) sz_log2p = (SZV == 8 ? 3 : 1) + group_shift - 6;
+    auto kernel = gemm_kernel<BM, BN, BITS, PAIR_SZ, SZV>;
     static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     kernel<<<dim3((unsigned)(tiles_m * tiles_n)), dim3(kGemmThreads), lds, stream>>>(
-        x, qweight, scales, zeros, y, m, n_out, n_in, group_shift, tiles_m, tiles_n);
+        x, qweight, scales, zeros, y, m, n_out, n_in, group_shift, tiles_m, tiles_n, sz_log2p);
     return hipGetLastError();
+}
+
+// Slices of one row and group per lane pair (PAIR_SZ): scale vectors of 8
+// groups where the rows' runs of groups are 16-byte aligned, else of 2 where
+// 4-byte aligned, for groups of 64 to 256 (a run then spans whole steps);
+// otherwise one gather per step.
+template <int BITS>
+hipError_t launch_paired(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                         const uint16_t *zeros, int m, int n_out, int n_in, int shift, uint16_t *y,
+                         hipStream_t stream)
+{
+    const int groups = shift >= 31 ? 1 : n_in >> shift;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros);
+    if (shift >= 6 && shift <= 8 && groups % 8 == 0 && (a & 15) == 0)
+        return launch_gemm<256, 128, BITS, true, 8>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream);
+    if (shift >= 6 && shift <= 8 && groups % 2 == 0 && (a & 3) == 0)
+        return launch_gemm<256, 128, BITS, true, 2>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream);
+    return launch_gemm<256, 128, BITS, true>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream);
 }
 
 }  // namespace
@@ -495,12 +572,11 @@ hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint
     while ((1 << shift) < group_size) ++shift;
     if ((1 << shift) != group_size) shift = 31;
     if (bits == 8)
-        return launch_gemm<256, 128, 8, true>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y,
-                                              stream);
+        return launch_paired<8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
     // INT4 slices hold 32 codes: with groups of 32 the two slices of a row
     // step belong to different groups
     if (group_size == 32)
         return launch_gemm<256, 128, 4, false>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y,
                                                stream);
-    return launch_gemm<256, 128, 4, true>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
+    return launch_paired<4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
 }
