@@ -100,10 +100,10 @@ constexpr int kGemmThreads = 64 * (kConsumers + kProducers);
 // loads the scale, the odd lane the zero-point, and a DPP swap gives each
 // lane both: one 2-byte gather per slice and step instead of two.
 // SZV > 1 (with PAIR_SZ, groups of 64..256): the lane loads the raw bits of
-// SZV consecutive groups of its row at once, every sz_log2p-th power of two
-// steps, and keeps them in registers.  The per-step 2-byte gathers, each
-// touching a line per row, were a sixth of the workgroup's L2 requests and
-// cost about 15 % of the step time.
+// SZV consecutive groups of its row at once, once every 2^sz_log2p steps
+// (the steps those groups span), and keeps them in registers.  Gathering 2
+// bytes per step instead, each wave instruction touching a line per row, made
+// up a sixth of the workgroup's L2 requests and about 15 % of the step time.
 template <int BM, int BN, int BITS, bool PAIR_SZ, int SZV = 1>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
