@@ -23,13 +23,14 @@
 // bit-exact; only alpha != 0.5 (powf) may differ from another libm by an ulp.
 //
 // GEMM tiling follows the W4A16 kernel (q4_gemm.hip) without the
-// dequantization: 256 x 128 output tiles, 4 waves stacked along m (64 x 128
-// each), k in steps of 128 bytes = four v_mfma_i32_32x32x32_i8 substeps,
-// three LDS stages of (x tile | weight tile) with one barrier per step, three
-// register sets of global loads issued three steps ahead, the XCD-aware tile
-// order and the conflict-free chunk swizzle of gemm_tile.h.  The MFMAs take
-// the weight fragment first, so each lane holds runs of 4 consecutive output
-// channels and the epilogue stores whole rows through LDS.
+// dequantization: 256 x 128 output tiles, k in steps of 128 bytes = four
+// v_mfma_i32_32x32x32_i8 substeps, three LDS stages of (x tile | weight tile)
+// with one barrier per step, warp specialization (four consumer waves stacked
+// along m, 64 x 128 each, and four producer waves that move both tiles by
+// direct global->LDS loads), the XCD-aware tile order and the conflict-free
+// chunk swizzle of gemm_tile.h.  The MFMAs take the weight fragment first, so
+// each lane holds runs of 4 consecutive output channels and the epilogue
+// stores whole rows through LDS.
 #include <type_traits>
 
 #include "gemm_tile.h"
@@ -235,21 +236,27 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
 // ---------------------------------------------------------------------------
 // int8 GEMM.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void w8a8_gemm_kernel(
+// Warp-specialized form: four consumer waves (fragment reads and MFMAs
+// only) and four producer waves per workgroup, two waves per SIMD.  With no
+// dequantization the producers only issue direct global->LDS loads
+// (buffer_load ... lds: no registers, no LDS store instructions) of step
+// k+2's x and weight tiles into stage (k+2) % 3 and wait for them before the
+// step's barrier; lane i of a load lands at row i / 8, physical chunk i % 8
+// and fetches the logical chunk that the row's swizzle places there.
+template <int BM, int BN>
+__global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
     const int8_t *__restrict__ qx, const float *__restrict__ sx, const int8_t *__restrict__ qw,
     const float *__restrict__ sw, uint16_t *__restrict__ y, int m, int n_out, int k, int tiles_m, int tiles_n)
 {
-    constexpr int BK = 128, KSUB = 4;
-    constexpr int NW = WM * WN, THREADS = 64 * NW;
-    constexpr int WT_M = BM / WM, WT_N = BN / WN;
+    constexpr int BK = 128, NC = 4, THREADS = 512;     // BK: four 32-wide substeps
+    constexpr int WT_M = BM / NC, WT_N = BN;
     constexpr int TM = WT_M / 32, TN = WT_N / 32;
-    constexpr int A_CHUNKS = BM * 8 / THREADS, B_CHUNKS = BN * 8 / THREADS;
-    constexpr int A_PART = A_CHUNKS / KSUB, B_PART = B_CHUNKS / KSUB;
-    static_assert(A_PART * KSUB == A_CHUNKS && B_PART * KSUB == B_CHUNKS, "tiles do not split evenly");
+    constexpr int XL = BM / NC / 8, WL = BN / NC / 8;    // direct loads per producer wave per step
     static_assert(TM * 32 == WT_M && TN * 32 == WT_N, "wave tile not a multiple of 32");
-    static_assert(THREADS % 128 == 0, "row swizzles assume 16-row lane strides");
+    static_assert(XL * 8 * NC == BM && WL * 8 * NC == BN, "tile rows do not split over the producers");
     constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
+    constexpr int A_CHUNKS = BM * 8 / THREADS, B_CHUNKS = BN * 8 / THREADS;   // tail step, all threads
+    static_assert(kStages == 3, "the loop is unrolled for three stages");
     static_assert(kStages * STAGE <= 160 * 1024, "stages exceed LDS");
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -259,7 +266,6 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_gemm_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave_m = wave / WN, wave_n = wave % WN;
     const int ksteps = k / BK, krem = k % BK;
 
     // Per-tile buffer resources; rows past m or n_out read the last row (never stored).
@@ -268,64 +274,12 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_gemm_kernel(
         const_cast<int8_t *>(qx + (int64_t)m0 * k), (short)0, rows_m * k, kBufferFlags);
     const __amdgpu_buffer_rsrc_t wr_ = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t *>(qw + (int64_t)n0 * k), (short)0, rows_n * k, kBufferFlags);
-    uint32_t xoff[A_CHUNKS], woff[B_CHUNKS];
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-        const int c = tid + i * THREADS;                   // row c / 8, chunk c % 8
-        xoff[i] = (uint32_t)min(c >> 3, rows_m - 1) * (uint32_t)k + (uint32_t)(c & 7) * 16u;
-    }
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-        const int c = tid + i * THREADS;
-        woff[i] = (uint32_t)min(c >> 3, rows_n - 1) * (uint32_t)k + (uint32_t)(c & 7) * 16u;
-    }
-    // LDS: chunk i of this lane sits THREADS / 8 rows (a multiple of 16) below chunk 0
-    const int st_row = tid >> 3;
-    const uint32_t a_st = st_row * 128 + (((tid & 7) ^ swz(st_row)) * 16);
-    const uint32_t b_st = A_BYTES + a_st;
-    const int frow = lane & 31, fkg = lane >> 5, fswz = swz(frow);
-    const uint32_t fa = (wave_m * WT_M + frow) * 128, fb = A_BYTES + (wave_n * WT_N + frow) * 128;
 
-    struct Regs {
-        u32x4 a[A_CHUNKS];
-        u32x4 b[B_CHUNKS];
-    };
     struct Frag {
         i32x4 a[TM], b[TN];
     };
-
-    auto load_part = [&](Regs &g, int kt, int p) {
-#pragma unroll
-        for (int q = 0; q < A_PART; ++q) {
-            const int i = p * A_PART + q;
-            g.a[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * BK, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < B_PART; ++q) {
-            const int i = p * B_PART + q;
-            g.b[i] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * BK, 0);
-        }
-    };
-    auto load_all = [&](Regs &g, int kt) {
-#pragma unroll
-        for (int p = 0; p < KSUB; ++p) load_part(g, kt, p);
-    };
-    auto store_part = [&](const Regs &g, uint32_t buf, int p) {
-#pragma unroll
-        for (int q = 0; q < A_PART; ++q) {
-            const int i = p * A_PART + q;
-            *reinterpret_cast<u32x4 *>(smem + buf + a_st + i * THREADS * 16) = g.a[i];
-        }
-#pragma unroll
-        for (int q = 0; q < B_PART; ++q) {
-            const int i = p * B_PART + q;
-            *reinterpret_cast<u32x4 *>(smem + buf + b_st + i * THREADS * 16) = g.b[i];
-        }
-    };
-    auto store_all = [&](const Regs &g, uint32_t buf) {
-#pragma unroll
-        for (int p = 0; p < KSUB; ++p) store_part(g, buf, p);
-    };
+    const int frow = lane & 31, fkg = lane >> 5, fswz = swz(frow);
+    const uint32_t fa = (wave * WT_M + frow) * 128, fb = A_BYTES + frow * 128;
     // Fragments of substep ks: lane (row l % 32, k group l / 32) reads chunk 2 ks + l / 32.
     auto read_frag = [&](Frag &f, uint32_t buf, int ks) {
         const uint32_t cofs = ((2 * ks + fkg) ^ fswz) * 16;
@@ -334,7 +288,6 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const i32x4 *>(smem + buf + fb + cofs + j * 32 * 128);
     };
-
     i32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -349,129 +302,161 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_gemm_kernel(
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
-    constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
 
-    if (ksteps > 0) {
-        Regs R[3];
-        Frag f0, f1;
-        const int kmax = ksteps - 1;
-        // loads in the loop's own order so the loop-head wait counts stay deep
-        load_all(R[0], 0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_all(R[1], min(1, kmax));
-        __builtin_amdgcn_sched_barrier(0);
-        load_all(R[2], min(2, kmax));
-        __builtin_amdgcn_sched_barrier(0);
-        store_all(R[0], 0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_all(R[0], min(3, kmax));
-        __builtin_amdgcn_sched_barrier(0);
-        store_all(R[1], STAGE);
-        __builtin_amdgcn_sched_barrier(0);
-        load_all(R[1], min(4, kmax));
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        read_frag(f0, 0, 0);
-
-        // Step k (k % 3 == J): MFMAs from stage J, step k+2's registers into
-        // stage (J+2) % 3 and reloaded with step k+5, step k+1's first
-        // fragments from stage (J+1) % 3; one barrier.
-        auto step = [&](auto J_, int kk) {
-            constexpr int J = decltype(J_)::value;
-            constexpr uint32_t cur = J * STAGE, nxt = ((J + 1) % 3) * STAGE, wr = ((J + 2) % 3) * STAGE;
-            Regs &g = R[(J + 2) % 3];
-            const int kl = min(kk + 5, kmax);
-            read_frag(f1, cur, 1);
-            store_part(g, wr, 0);
-            load_part(g, kl, 0);
-            mma(f0);
-            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
-            __builtin_amdgcn_sched_barrier(0);
-            read_frag(f0, cur, 2);
-            store_part(g, wr, 1);
-            load_part(g, kl, 1);
-            mma(f1);
-            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
-            __builtin_amdgcn_sched_barrier(0);
-            read_frag(f1, cur, 3);
-            store_part(g, wr, 2);
-            load_part(g, kl, 2);
-            mma(f0);
-            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
-            __builtin_amdgcn_sched_barrier(0);
-            read_frag(f0, nxt, 0);
-            store_part(g, wr, 3);
-            load_part(g, kl, 3);
-            mma(f1);
-            interleave<0, NMFMA, NFRAG, A_PART + B_PART, A_PART + B_PART, 0>();
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-        };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        int kk = 0;
-        for (; kk + 3 <= ksteps; kk += 3) {
-            step(I0{}, kk);
-            step(I1{}, kk + 1);
-            step(I2{}, kk + 2);
+    if (wave < NC) {
+        // ---------------- consumer ----------------
+        if (ksteps > 0) {
+            __syncthreads();                            // stages 0 and 1 written
+            Frag f0, f1;
+            read_frag(f0, 0, 0);
+            // Step k (k % 3 == J): substeps 1..3 from stage J, then step
+            // k+1's first fragments from stage (J+1) % 3; one barrier.
+            auto step = [&](auto J_) {
+                constexpr int J = decltype(J_)::value;
+                constexpr uint32_t cur = J * STAGE, nxt = ((J + 1) % 3) * STAGE;
+                read_frag(f1, cur, 1);
+                mma(f0);
+                read_frag(f0, cur, 2);
+                mma(f1);
+                read_frag(f1, cur, 3);
+                mma(f0);
+                read_frag(f0, nxt, 0);
+                mma(f1);
+                __syncthreads();
+            };
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            int kk = 0;
+            for (; kk + 3 <= ksteps; kk += 3) {
+                step(I0{});
+                step(I1{});
+                step(I2{});
+            }
+            if (kk < ksteps) step(I0{});
+            if (kk + 1 < ksteps) step(I1{});
         }
-        if (kk < ksteps) step(I0{}, kk);
-        if (kk + 1 < ksteps) step(I1{}, kk + 1);
+    } else {
+        // ---------------- producer ----------------
+        typedef __attribute__((address_space(3))) char lds_char;
+        const int pw = wave - NC;
+        uint32_t xdoff[XL], wdoff[WL];
+#pragma unroll
+        for (int j = 0; j < XL; ++j) {
+            const int r = pw * XL * 8 + 8 * j + (lane >> 3);
+            xdoff[j] = (uint32_t)min(r, rows_m - 1) * (uint32_t)k + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < WL; ++j) {
+            const int r = pw * WL * 8 + 8 * j + (lane >> 3);
+            wdoff[j] = (uint32_t)min(r, rows_n - 1) * (uint32_t)k + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+        }
+        // (the offsets are passed as int explicitly: with an implicit
+        // conversion this toolchain's host pass dropped the kernel's launch stub)
+        auto load = [&](uint32_t buf, int kt) {
+            lds_char *dx = (lds_char *)smem + buf + pw * XL * 8 * 128;
+            lds_char *dw = (lds_char *)smem + buf + A_BYTES + pw * WL * 8 * 128;
+#pragma unroll
+            for (int j = 0; j < XL; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(dx + j * 8 * 128),
+                                                         16, (int)xdoff[j], kt * BK, 0, 0);
+#pragma unroll
+            for (int j = 0; j < WL; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr_, (__attribute__((address_space(3))) void *)(dw + j * 8 * 128),
+                                                         16, (int)wdoff[j], kt * BK, 0, 0);
+        };
+        if (ksteps > 0) {
+            const int kmax = ksteps - 1;
+            load(0, 0);
+            load(STAGE, min(1, kmax));
+            __syncthreads();                            // (waits for every load, direct ones included)
+            // Step k (k % 3 == J): step k+2 into stage (J+2) % 3, which the
+            // consumers finished reading before the previous barrier; steps
+            // past the last one rewrite the last step.
+            auto step = [&](auto J_, int kk) {
+                constexpr int J = decltype(J_)::value;
+                load(((J + 2) % 3) * STAGE, min(kk + 2, kmax));
+                __syncthreads();
+            };
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            int kk = 0;
+            for (; kk + 3 <= ksteps; kk += 3) {
+                step(I0{}, kk);
+                step(I1{}, kk + 1);
+                step(I2{}, kk + 2);
+            }
+            if (kk < ksteps) step(I0{}, kk);
+            if (kk + 1 < ksteps) step(I1{}, kk + 1);
+        }
     }
 
     if (krem) {
-        // Final partial step of krem = 32, 64 or 96 bytes: the chunks past
-        // krem are zero in LDS, so only krem / 32 substeps run.  Every wave
-        // passed the last barrier after its last LDS read, so stage 0 is free.
+        // Final partial step of krem = 32, 64 or 96 bytes, loaded by every
+        // thread: the chunks past krem are zero in LDS, so only krem / 32
+        // substeps run.  Every wave passed the last barrier after its last
+        // LDS access, so stage 0 is free.
         const int kt = ksteps;
+        const int st_row = tid >> 3;
+        const uint32_t a_st = st_row * 128 + (((tid & 7) ^ swz(st_row)) * 16);
         const bool valid = (tid & 7) * 16 < krem;
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
+            const int c = tid + i * THREADS;
+            const uint32_t off = (uint32_t)min(c >> 3, rows_m - 1) * (uint32_t)k + (uint32_t)(c & 7) * 16u;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (valid) v = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], kt * BK, 0);
+            if (valid) v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, kt * BK, 0);
             *reinterpret_cast<u32x4 *>(smem + a_st + i * THREADS * 16) = v;
         }
 #pragma unroll
         for (int i = 0; i < B_CHUNKS; ++i) {
+            const int c = tid + i * THREADS;
+            const uint32_t off = (uint32_t)min(c >> 3, rows_n - 1) * (uint32_t)k + (uint32_t)(c & 7) * 16u;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (valid) v = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[i], kt * BK, 0);
-            *reinterpret_cast<u32x4 *>(smem + b_st + i * THREADS * 16) = v;
+            if (valid) v = __builtin_amdgcn_raw_buffer_load_b128(wr_, off, kt * BK, 0);
+            *reinterpret_cast<u32x4 *>(smem + A_BYTES + a_st + i * THREADS * 16) = v;
         }
         __syncthreads();
-        for (int ks = 0; ks < krem / 32; ++ks) {
-            Frag f;
-            read_frag(f, 0, ks);
-            mma(f);
+        if (wave < NC) {
+            for (int ks = 0; ks < krem / 32; ++ks) {
+                Frag f;
+                read_frag(f, 0, ks);
+                mma(f);
+            }
         }
     }
 
     // Epilogue: tile (i, j) holds y^T -- lane l, register r is output channel
     // 8 (r / 4) + 4 (l / 32) + r % 4 of the tile's 32, for x row l % 32.
     // y = fp16((float(acc) * sx[row]) * sw[channel]) goes through LDS (rows
-    // padded to YS bytes) and leaves as 16-byte pieces of whole rows.
+    // padded to YS bytes) and leaves as 16-byte pieces of whole rows, stored
+    // by all eight waves.
     constexpr int YS = BN * 2 + 16;
     static_assert(BM * YS <= kStages * STAGE, "output tile exceeds LDS");
     __syncthreads();
+    if (wave < NC) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = wave_m * WT_M + i * 32 + (lane & 31);
-        const float sxv = sx[m0 + min(r, rows_m - 1)];
+        for (int i = 0; i < TM; ++i) {
+            const int r = wave * WT_M + i * 32 + (lane & 31);
+            const float sxv = sx[m0 + min(r, rows_m - 1)];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int c = wave_n * WT_N + j * 32 + 8 * rq + 4 * (lane >> 5);
-                float v[4];
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int c = j * 32 + 8 * rq + 4 * (lane >> 5);
+                    float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float swv = sw[n0 + min(c + e, rows_n - 1)];
-                    v[e] = ((float)acc[i][j][4 * rq + e] * sxv) * swv;
+                    for (int e = 0; e < 4; ++e) {
+                        const float swv = sw[n0 + min(c + e, rows_n - 1)];
+                        v[e] = ((float)acc[i][j][4 * rq + e] * sxv) * swv;
+                    }
+                    const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]};
+                    const f16x2 hi = {(_Float16)v[2], (_Float16)v[3]};
+                    *reinterpret_cast<u32x2 *>(smem + r * YS + c * 2) =
+                        u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
                 }
-                const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]};
-                const f16x2 hi = {(_Float16)v[2], (_Float16)v[3]};
-                *reinterpret_cast<u32x2 *>(smem + r * YS + c * 2) = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
-            }
+        }
     }
     __syncthreads();
     constexpr int CPR = BN / 8;
@@ -557,13 +542,13 @@ hipError_t w8a8_launch_quant_act(const uint16_t *x, const float *s, int64_t m, i
 hipError_t w8a8_launch_gemm(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw, int64_t m,
                             int64_t n_out, int64_t k, uint16_t *y, hipStream_t stream)
 {
-    constexpr int BM = 256, BN = 128, WM = 4, WN = 1;
+    constexpr int BM = 256, BN = 128;
     const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n_out + BN - 1) / BN);
-    auto kernel = w8a8_gemm_kernel<BM, BN, WM, WN>;
+    auto kernel = w8a8_gemm_ws_kernel<BM, BN>;
     const hipError_t e = allow_full_lds(kernel);
     if (e != hipSuccess) return e;
     const size_t lds = kStages * (size_t)(BM + BN) * 128;
-    kernel<<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, lds, stream>>>(qx, sx, qw, sw, y, (int)m, (int)n_out,
-                                                                          (int)k, tiles_m, tiles_n);
+    kernel<<<(unsigned)(tiles_m * tiles_n), 512, lds, stream>>>(qx, sx, qw, sw, y, (int)m, (int)n_out, (int)k,
+                                                               tiles_m, tiles_n);
     return hipGetLastError();
 }
