@@ -70,6 +70,18 @@ def time_graph(graph, steps, warmup):
     return start.elapsed_time(end) * 1e-3, wall
 
 
+def settle(graph, seconds=0.25):
+    """Untimed replays for at least `seconds`: under MFMA load the clock settles
+    at its loaded value only after some 0.1 s, and the first replays after a
+    lighter phase run up to 20 % slower."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        graph.replay()
+        torch.cuda.synchronize()
+
+
 def time_graph_eager(fn, steps, warmup):
     """HIP-event time of `steps` eager calls of fn (large kernels: launch cost
     is negligible next to them)."""
@@ -235,6 +247,7 @@ def bench_prefill(args, dev):
         y = torch.empty((syn.PREFILL_M, lin.n_out), dtype=torch.float16, device=dev)
         reps = 20
         g = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
+        settle(g)
         el, _ = time_graph(g, 5, 3)
         t = el / (5 * reps)
         flop = 2 * syn.PREFILL_M * lin.n_out * lin.n_in
@@ -345,6 +358,7 @@ def bench_int8(args, dev):
         y = torch.empty((syn.PREFILL_M, pl.n_out), dtype=torch.float16, device=dev)
         reps = 20
         gr = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
+        settle(gr)
         el, _ = time_graph(gr, 5, 3)
         t = el / (5 * reps)
         flop = 2 * syn.PREFILL_M * pl.n_out * pl.n_in
@@ -432,6 +446,7 @@ def bench_w8a8(args, dev):
         y = torch.empty((syn.PREFILL_M, lin.n_out), dtype=torch.float16, device=dev)
         reps = 20
         g = capture(lambda: [w8a8.gemm(qx, sx, layer.qw, layer.sw, y) for _ in range(reps)])
+        settle(g)
         el, _ = time_graph(g, 5, 3)
         t = el / (5 * reps)
         gl = capture(lambda: [(w8a8.quantize_act(x, layer.s, qx, sx), w8a8.gemm(qx, sx, layer.qw, layer.sw, y))
