@@ -28,10 +28,11 @@
 //     loads (buffer_load ... lds: no registers, no LDS store instructions,
 //     which gfx950 executes at well under half its LDS read rate), weights
 //     from one of three register sets loaded three steps earlier, which is
-//     then reloaded with step k+5.  Before the barrier a producer waits
-//     only until the step's x loads (and every older load) have landed,
-//     leaving the new weight loads in flight; a barrier that waited for
-//     every load would empty the pipeline each step.
+//     then reloaded with step k+5 (scales and zero-points: see SZV below).
+//     Before the barrier a producer waits only until the step's x loads
+//     (and every older load) have landed, leaving the new weight loads in
+//     flight; a barrier that waited for every load would empty the pipeline
+//     each step.
 // Both rotations have period three, so the loop is unrolled three times and
 // every LDS address is a lane constant plus an immediate.  Global loads are
 // buffer loads: a per-tile resource, a lane-constant 32-bit offset and a
