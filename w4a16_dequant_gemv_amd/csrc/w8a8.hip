@@ -23,14 +23,17 @@
 // bit-exact; only alpha != 0.5 (powf) may differ from another libm by an ulp.
 //
 // GEMM tiling follows the W4A16 kernel (q4_gemm.hip) without the
-// dequantization: 256 x 128 output tiles, k in steps of 128 bytes = four
-// v_mfma_i32_32x32x32_i8 substeps, three LDS stages of (x tile | weight tile)
+// dequantization: 256 x 128 output tiles, k in steps of 128 bytes = two
+// v_mfma_i32_16x16x64_i8 substeps, three LDS stages of (x tile | weight tile)
 // with one barrier per step, warp specialization (four consumer waves stacked
 // along m, 64 x 128 each, and four producer waves that move both tiles by
 // direct global->LDS loads), the XCD-aware tile order and the conflict-free
 // chunk swizzle of gemm_tile.h.  The MFMAs take the weight fragment first, so
 // each lane holds runs of 4 consecutive output channels and the epilogue
-// stores whole rows through LDS.
+// stores whole rows through LDS.  With the consumers' instruction streams
+// holding only fragment reads and MFMAs, the 16x16x64 form measured 3-8 %
+// faster than v_mfma_i32_32x32x32_i8 (same operand bytes per op); in the
+// earlier kernel, where every wave also loaded and stored, it was slower.
 #include <type_traits>
 
 #include "gemm_tile.h"
@@ -248,11 +251,11 @@ __global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
     const int8_t *__restrict__ qx, const float *__restrict__ sx, const int8_t *__restrict__ qw,
     const float *__restrict__ sw, uint16_t *__restrict__ y, int m, int n_out, int k, int tiles_m, int tiles_n)
 {
-    constexpr int BK = 128, NC = 4, THREADS = 512;     // BK: four 32-wide substeps
+    constexpr int BK = 128, NC = 4, THREADS = 512;     // BK: two 64-wide substeps
     constexpr int WT_M = BM / NC, WT_N = BN;
-    constexpr int TM = WT_M / 32, TN = WT_N / 32;
+    constexpr int TM = WT_M / 16, TN = WT_N / 16;
     constexpr int XL = BM / NC / 8, WL = BN / NC / 8;    // direct loads per producer wave per step
-    static_assert(TM * 32 == WT_M && TN * 32 == WT_N, "wave tile not a multiple of 32");
+    static_assert(TM * 16 == WT_M && TN * 16 == WT_N, "wave tile not a multiple of 16");
     static_assert(XL * 8 * NC == BM && WL * 8 * NC == BN, "tile rows do not split over the producers");
     constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
     constexpr int A_CHUNKS = BM * 8 / THREADS, B_CHUNKS = BN * 8 / THREADS;   // tail step, all threads
@@ -278,29 +281,29 @@ __global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
     struct Frag {
         i32x4 a[TM], b[TN];
     };
-    const int frow = lane & 31, fkg = lane >> 5, fswz = swz(frow);
+    const int frow = lane & 15, fkg = lane >> 4, fswz = swz(frow);
     const uint32_t fa = (wave * WT_M + frow) * 128, fb = A_BYTES + frow * 128;
-    // Fragments of substep ks: lane (row l % 32, k group l / 32) reads chunk 2 ks + l / 32.
+    // Fragments of substep ks (64 k): lane (row l % 16, k group l / 16) reads chunk 4 ks + l / 16.
     auto read_frag = [&](Frag &f, uint32_t buf, int ks) {
-        const uint32_t cofs = ((2 * ks + fkg) ^ fswz) * 16;
+        const uint32_t cofs = ((4 * ks + fkg) ^ fswz) * 16;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const i32x4 *>(smem + buf + fa + cofs + i * 32 * 128);
+        for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const i32x4 *>(smem + buf + fa + cofs + i * 16 * 128);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const i32x4 *>(smem + buf + fb + cofs + j * 32 * 128);
+        for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const i32x4 *>(smem + buf + fb + cofs + j * 16 * 128);
     };
-    i32x16 acc[TM][TN];
+    i32x4 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0;
     auto mma = [&](const Frag &f) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
 
     if (wave < NC) {
@@ -309,16 +312,12 @@ __global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
             __syncthreads();                            // stages 0 and 1 written
             Frag f0, f1;
             read_frag(f0, 0, 0);
-            // Step k (k % 3 == J): substeps 1..3 from stage J, then step
-            // k+1's first fragments from stage (J+1) % 3; one barrier.
+            // Step k (k % 3 == J): substep 1 from stage J, then step k+1's
+            // first fragments from stage (J+1) % 3; one barrier.
             auto step = [&](auto J_) {
                 constexpr int J = decltype(J_)::value;
                 constexpr uint32_t cur = J * STAGE, nxt = ((J + 1) % 3) * STAGE;
                 read_frag(f1, cur, 1);
-                mma(f0);
-                read_frag(f0, cur, 2);
-                mma(f1);
-                read_frag(f1, cur, 3);
                 mma(f0);
                 read_frag(f0, nxt, 0);
                 mma(f1);
@@ -394,8 +393,8 @@ __global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
 
     if (krem) {
         // Final partial step of krem = 32, 64 or 96 bytes, loaded by every
-        // thread: the chunks past krem are zero in LDS, so only krem / 32
-        // substeps run.  Every wave passed the last barrier after its last
+        // thread: the chunks past krem are zero in LDS, so the substeps that
+        // hold data run (one for krem <= 64, two for 96).  Every wave passed the last barrier after its last
         // LDS access, so stage 0 is free.
         const int kt = ksteps;
         const int st_row = tid >> 3;
@@ -419,7 +418,7 @@ __global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
         }
         __syncthreads();
         if (wave < NC) {
-            for (int ks = 0; ks < krem / 32; ++ks) {
+            for (int ks = 0; ks < (krem + 63) / 64; ++ks) {
                 Frag f;
                 read_frag(f, 0, ks);
                 mma(f);
@@ -428,7 +427,7 @@ __global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
     }
 
     // Epilogue: tile (i, j) holds y^T -- lane l, register r is output channel
-    // 8 (r / 4) + 4 (l / 32) + r % 4 of the tile's 32, for x row l % 32.
+    // 4 (l / 16) + r of the tile's 16, for x row l % 16.
     // y = fp16((float(acc) * sx[row]) * sw[channel]) goes through LDS (rows
     // padded to YS bytes) and leaves as 16-byte pieces of whole rows, stored
     // by all eight waves.
@@ -438,24 +437,22 @@ __global__ __launch_bounds__(512) void w8a8_gemm_ws_kernel(
     if (wave < NC) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int r = wave * WT_M + i * 32 + (lane & 31);
+            const int r = wave * WT_M + i * 16 + (lane & 15);
             const float sxv = sx[m0 + min(r, rows_m - 1)];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j) {
+                const int c = j * 16 + 4 * (lane >> 4);
+                float v[4];
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int c = j * 32 + 8 * rq + 4 * (lane >> 5);
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float swv = sw[n0 + min(c + e, rows_n - 1)];
-                        v[e] = ((float)acc[i][j][4 * rq + e] * sxv) * swv;
-                    }
-                    const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]};
-                    const f16x2 hi = {(_Float16)v[2], (_Float16)v[3]};
-                    *reinterpret_cast<u32x2 *>(smem + r * YS + c * 2) =
-                        u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+                for (int e = 0; e < 4; ++e) {
+                    const float swv = sw[n0 + min(c + e, rows_n - 1)];
+                    v[e] = ((float)acc[i][j][e] * sxv) * swv;
                 }
+                const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]};
+                const f16x2 hi = {(_Float16)v[2], (_Float16)v[3]};
+                *reinterpret_cast<u32x2 *>(smem + r * YS + c * 2) =
+                    u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+            }
         }
     }
     __syncthreads();
