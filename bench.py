@@ -13,8 +13,9 @@ fp16 scales and zero-points (4/g B/weight), x and y once per linear.
 Also measured in the same run and reported as extra keys:
   prefill  -- q4_gemm at m=2048 on the three 7B projection shapes (TFLOP/s),
   decode70b -- q4_gemv at m=8 over 80 layers of 70B-shaped linears (GB/s),
-  stress   -- q4_gemv at m=1 on 8192x28672 for g=128 and g=32 (GB/s),
-  quantize -- q4_quantize_pack and q4_dequant on 8192x28672 (GB/s),
+  stress   -- 8192x28672 Student-t weights with constant and zero groups,
+              g=128 and g=32, asymmetric and symmetric: quantize+pack,
+              dequant and the m=1 GEMV (GB/s),
   single_gemv_4096x4096 -- one 4096x4096 linear at m=1 over 64 packed copies,
   w8a16    -- INT8 decode (8 fused 7B layers, per-channel) and prefill (g=128),
   kv_codec -- the KV-cache codec on one 70B-shaped layer cache (GB/s) and the
@@ -23,12 +24,19 @@ Also measured in the same run and reported as extra keys:
               the whole smoothed layer (activation quantization + product),
   gptq_awq -- GPTQ and AWQ on one 4096x4096 linear: time per layer and the
               output error relative to plain rounding,
-  cpu_baseline -- the CPU oracle (dequantize + binary64 product) timed on
-                  this host's cores on a bounded sample of the decode step.
+  cpu_baseline -- the CPU oracle timed on this host's cores on bounded samples
+              of each workload (its figure for a workload also sits next to
+              the GPU figure, as `oracle_*` keys).
+
+The inputs of every timed linear-layer call are built by the functions in the
+"workloads" section below; `timed_linear_calls()` lists those calls, and the
+parity tests run the oracle on exactly these inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+       python bench.py --trace-summary CSV [--last N]   (rocprofv3 kernel trace)
 """
 import argparse
+import collections
 import hashlib
 import json
 import os
@@ -54,6 +62,146 @@ def algorithmic_bytes(n_out, n_in, m, g, bits=4):
     return n_out * n_in * bits // 8 + 4 * n_out * (n_in // g) + 2 * m * n_in + 2 * m * n_out
 
 
+def quantize_bytes(n_out, n_in, g, bits=4):
+    """Bytes a quantize+pack (or dequant) pass moves: fp32 weights one way,
+    packed codes and fp16 scale and zero-point the other."""
+    return n_out * n_in * 4 + n_out * n_in * bits // 8 + 4 * n_out * (n_in // g)
+
+
+# ---------------------------------------------------------------------------
+# Workloads: the inputs of every timed linear-layer call.
+# ---------------------------------------------------------------------------
+Call = collections.namedtuple("Call", "leg index kind bits m n_out n_in group_size symmetric")
+
+STRESS_SHAPE = (8192, 28672)
+SINGLE_COPIES = 64
+
+
+def decode7b_weight(layer, j, dev):
+    """fp32 weights of fused linear j (qkv, o, gate_up, down) of 7B layer `layer`."""
+    import torch
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    lin = syn.LLAMA7B_LINEARS
+    _, idx = syn.FUSED_LAYOUT[j]
+    return torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama7b_seed(layer, i), 0.02,
+                                               syn.n_outliers(lin[i].n_in), dev) for i in idx])
+
+
+def decode7b_x(j, dev, int8=False):
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    n_in = syn.fused_linears(syn.LLAMA7B_LINEARS)[j].n_in
+    return syn.activations_f16_device(1, n_in, (2200 if int8 else 2100) + j, dev)
+
+
+def split_of(i):
+    """Linear i of a 7B layer -> (fused index, first row within it)."""
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    for j, (_, idx) in enumerate(syn.FUSED_LAYOUT):
+        if i in idx:
+            return j, sum(syn.LLAMA7B_LINEARS[t].n_out for t in idx[:idx.index(i)])
+    raise ValueError(i)
+
+
+def decode70b_weight(layer, j, dev):
+    import torch
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    lin = syn.LLAMA70B_LINEARS
+    _, idx = syn.FUSED_LAYOUT[j]
+    return torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama70b_seed(layer, i), 0.015, 0, dev)
+                      for i in idx])
+
+
+def decode70b_x(j, dev):
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    return syn.activations_f16_device(8, syn.fused_linears(syn.LLAMA70B_LINEARS)[j].n_in, 3100 + j, dev)
+
+
+def stress_weight(g, dev):
+    """8192x28672 = 0.02 * Student-t(3), 1 % constant and 0.1 % zero groups of g."""
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    return syn.student_t_weight_device(*STRESS_SHAPE, 5, g, dev)
+
+
+def stress_x(dev):
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    return syn.activations_f16_device(1, STRESS_SHAPE[1], 5100, dev)
+
+
+def single_weight(dev):
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    return syn.normal_weight_device(4096, 4096, 1, 0.02, 8, dev)
+
+
+def single_copy(w, c):
+    """Copy c of the 4096x4096 weights cycled by the single-linear leg."""
+    return w.mul(1.0 + c * 1e-3) if c else w
+
+
+def single_x(dev):
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    return syn.activations_f16_device(1, 4096, 101, dev)
+
+
+def prefill_weight(i, dev):
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    pl = syn.PREFILL_LINEARS[i]
+    return syn.normal_weight_device(pl.n_out, pl.n_in, 4000 + i, 0.02, syn.n_outliers(pl.n_in), dev)
+
+
+def prefill_x(i, dev):
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    return syn.activations_f16_device(syn.PREFILL_M, syn.PREFILL_LINEARS[i].n_in, 4100 + i, dev)
+
+
+def timed_linear_calls():
+    """Every linear-layer call the benchmark times, with the workload that
+    builds its inputs (leg, index).  The benchmark checks at run time that it
+    makes no other call."""
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    out = []
+    for j, lin in enumerate(syn.fused_linears(syn.LLAMA7B_LINEARS)):
+        out.append(Call("decode7b", j, "gemv", 4, 1, lin.n_out, lin.n_in, 128, False))
+        out.append(Call("w8a16_decode", j, "gemv", 8, 1, lin.n_out, lin.n_in, lin.n_in, False))
+    for i, lin in enumerate(syn.LLAMA7B_LINEARS):
+        out.append(Call("decode7b_split", i, "gemv", 4, 1, lin.n_out, lin.n_in, 128, False))
+    for j, lin in enumerate(syn.fused_linears(syn.LLAMA70B_LINEARS)):
+        out.append(Call("decode70b", j, "gemv", 4, 8, lin.n_out, lin.n_in, 128, False))
+    for g in (128, 32):
+        for sym in (False, True):
+            out.append(Call("stress", 0, "gemv", 4, 1, *STRESS_SHAPE, g, sym))
+    out.append(Call("single", 0, "gemv", 4, 1, 4096, 4096, 128, False))
+    for i, pl in enumerate(syn.PREFILL_LINEARS):
+        out.append(Call("prefill", i, "gemm", 4, syn.PREFILL_M, pl.n_out, pl.n_in, 128, False))
+        out.append(Call("w8a16_prefill", i, "gemm", 8, syn.PREFILL_M, pl.n_out, pl.n_in, 128, False))
+    return out
+
+
+# Calls made while capturing the timed graphs: (kind, bits, m, n_out, n_in, group_size).
+_MADE = set()
+
+
+def gemv(x, qw, y):
+    import w4a16_dequant_gemv_amd as w4
+    _MADE.add(("gemv", qw.bits, x.shape[0], qw.n_out, qw.n_in, qw.group_size))
+    return w4.gemv(x, qw, y)
+
+
+def gemm(x, qw, y):
+    import w4a16_dequant_gemv_amd as w4
+    _MADE.add(("gemm", qw.bits, x.shape[0], qw.n_out, qw.n_in, qw.group_size))
+    return w4.gemm(x, qw, y)
+
+
+def check_calls():
+    known = {(c.kind, c.bits, c.m, c.n_out, c.n_in, c.group_size) for c in timed_linear_calls()}
+    extra = _MADE - known
+    if extra:
+        raise RuntimeError(f"timed calls missing from timed_linear_calls(): {sorted(extra)}")
+
+
+# ---------------------------------------------------------------------------
+# Timing helpers.
+# ---------------------------------------------------------------------------
 def time_graph(graph, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -138,43 +286,32 @@ def counters_traffic(bytes_per_launch):
 
 
 # ---------------------------------------------------------------------------
-def build_decode_stack(layers, dev, keep_host_layer0):
-    """Quantized 7B-shaped layers stored the way serving engines store them:
-    q, k, v concatenated into one [12288, 4096] matrix and gate, up into one
-    [22016, 4096] matrix (quantization is per row, so this equals quantizing
-    each linear alone).  Each of the four GEMVs of a layer has its own x."""
+# GPU legs.
+# ---------------------------------------------------------------------------
+def bench_decode(args, dev, host):
     import torch
     import w4a16_dequant_gemv_amd as w4
     from w4a16_dequant_gemv_amd import synthetic as syn
-    lin = syn.LLAMA7B_LINEARS
-    fused = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
-    xs = {name: syn.activations_f16_device(1, lin[idx[0]].n_in, 2100 + j, dev)
-          for j, (name, idx) in enumerate(fused)}
-    gemvs, host_w = [], []
-    for layer in range(layers):
-        for name, idx in fused:
-            w = torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama7b_seed(layer, i),
-                                                    0.02, syn.n_outliers(lin[i].n_in), dev) for i in idx])
-            qw = w4.quantize_pack(w, 128)
-            if layer == 0 and keep_host_layer0:
-                host_w.append((name, w.cpu().numpy(), xs[name].cpu().numpy()))
-            del w
-            y = torch.empty((1, qw.n_out), dtype=torch.float16, device=dev)
-            gemvs.append((name, qw, xs[name], y))
-    torch.cuda.synchronize()
-    return gemvs, host_w
-
-
-def bench_decode(args, dev):
-    import w4a16_dequant_gemv_amd as w4
-    layers = 32
+    from w4a16_dequant_gemv_amd.api import QuantizedWeight
+    layers = syn.LLAMA7B_LAYERS
     t0 = time.perf_counter()
-    gemvs, host_w = build_decode_stack(layers, dev, keep_host_layer0=not args.no_cpu_baseline)
+    fused = syn.fused_linears(syn.LLAMA7B_LINEARS)
+    xs = [decode7b_x(j, dev) for j in range(len(fused))]
+    gemvs = []
+    for layer in range(layers):
+        for j, lin in enumerate(fused):
+            w = decode7b_weight(layer, j, dev)
+            qw = w4.quantize_pack(w, 128)
+            if layer == 0 and host is not None:
+                host.setdefault("decode7b", []).append((lin.name, w.cpu().numpy(), xs[j].cpu().numpy()))
+            del w
+            gemvs.append((lin.name, qw, xs[j], torch.empty((1, qw.n_out), dtype=torch.float16, device=dev)))
+    torch.cuda.synchronize()
     log(f"decode stack: {layers} layers x 7 linears quantized in {time.perf_counter() - t0:.1f} s")
 
     def step():
         for _, qw, x, y in gemvs:
-            w4.gemv(x, qw, y)
+            gemv(x, qw, y)
 
     graph = capture(step)
     step_bytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 1, 128) for _, qw, _, _ in gemvs)
@@ -188,65 +325,36 @@ def bench_decode(args, dev):
                bytes_per_launch=step_bytes / launches)
     # The same weights with one launch per linear (7 per layer): row slices
     # of the fused matrices are themselves valid packed weights.
-    from w4a16_dequant_gemv_amd.api import QuantizedWeight
-    split = {"qkv": (4096, 4096, 4096), "gate_up": (11008, 11008)}
-    per_linear = []
-    for name, qw, x, y in gemvs:
-        off = 0
-        for n in split.get(name, (qw.n_out,)):
-            sl = slice(off, off + n)
-            per_linear.append((QuantizedWeight(qw.qweight[sl], qw.scales[sl], qw.zeros[sl], n, qw.n_in, 128),
-                               x, y[:, sl]))
-            off += n
     res["gbs_7_launches_per_layer"] = None
     if not args.decode_only:
-        graph7 = capture(lambda: [w4.gemv(x, q, y) for q, x, y in per_linear])
+        per_linear = []
+        for layer in range(layers):
+            for i, lin in enumerate(syn.LLAMA7B_LINEARS):
+                j, off = split_of(i)
+                _, qw, x, y = gemvs[layer * len(fused) + j]
+                sl = slice(off, off + lin.n_out)
+                per_linear.append((QuantizedWeight(qw.qweight[sl], qw.scales[sl], qw.zeros[sl], lin.n_out, qw.n_in,
+                                                   128), x, y[:, sl]))
+        graph7 = capture(lambda: [gemv(x, q, y) for q, x, y in per_linear])
         el7, _ = time_graph(graph7, max(1, args.steps // 2), 1)
         res["gbs_7_launches_per_layer"] = round(step_bytes * max(1, args.steps // 2) / el7 / 1e9, 1)
         del graph7
-    return res, host_w
+    return res
 
 
-def cpu_baseline(host_w, budget_s):
-    """Oracle GEMV (dequantize, then binary64 product) on layer 0's four
-    fused linears, repeated until about `budget_s` seconds of CPU work."""
-    import numpy as np
-    import oracle
-    orc = oracle.load()
-    prepared = []
-    for name, w, x in host_w:
-        packed, scales, zeros, _ = orc.quantize_pack(w, 128)      # untimed preparation
-        prepared.append((name, packed, scales, zeros, x.view(np.uint16)))
-    done_bytes, t_cpu, n_lin = 0, 0.0, 0
-    while t_cpu < budget_s:
-        for name, packed, scales, zeros, x in prepared:
-            t0 = time.perf_counter()
-            orc.linear_from_packed(x, packed, scales, zeros, 128)
-            t_cpu += time.perf_counter() - t0
-            done_bytes += algorithmic_bytes(packed.shape[0], packed.shape[1] * 8, 1, 128)
-            n_lin += 1
-            if t_cpu >= budget_s:
-                break
-    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    return dict(value=round(done_bytes / t_cpu / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
-                sample=(f"{n_lin} fused decode GEMVs of the 7B layer-0 shapes (qkv 12288x4096, o 4096x4096, "
-                        f"gate_up 22016x4096, down 4096x11008; m=1, g=128) through the C oracle's "
-                        f"dequantize + binary64 product, {t_cpu:.1f} s of CPU time"))
-
-
-def bench_prefill(args, dev):
+def bench_prefill(args, dev, bits=4):
     import torch
     import w4a16_dequant_gemv_amd as w4
     from w4a16_dequant_gemv_amd import synthetic as syn
     out, tot_flop, tot_t = [], 0, 0.0
     for i, lin in enumerate(syn.PREFILL_LINEARS):
-        w = syn.normal_weight_device(lin.n_out, lin.n_in, 4000 + i, 0.02, syn.n_outliers(lin.n_in), dev)
-        qw = w4.quantize_pack(w, 128)
+        w = prefill_weight(i, dev)
+        qw = w4.quantize_pack(w, 128, bits=bits)
         del w
-        x = syn.activations_f16_device(syn.PREFILL_M, lin.n_in, 4100 + i, dev)
+        x = prefill_x(i, dev)
         y = torch.empty((syn.PREFILL_M, lin.n_out), dtype=torch.float16, device=dev)
         reps = 20
-        g = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
+        g = capture(lambda: [gemm(x, qw, y) for _ in range(reps)])
         settle(g)
         el, _ = time_graph(g, 5, 3)
         t = el / (5 * reps)
@@ -255,6 +363,8 @@ def bench_prefill(args, dev):
                         tflops=round(flop / t / 1e12, 1)))
         tot_flop += flop
         tot_t += t
+        del qw, x, y, g
+    torch.cuda.empty_cache()
     return dict(shapes=out, tflops=round(tot_flop / tot_t / 1e12, 1))
 
 
@@ -265,22 +375,19 @@ def bench_decode70b(args, dev):
     import w4a16_dequant_gemv_amd as w4
     from w4a16_dequant_gemv_amd import synthetic as syn
     layers = syn.LLAMA70B_LAYERS if not args.quick else 8
-    lin = syn.LLAMA70B_LINEARS
-    fused = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
-    xs = {name: syn.activations_f16_device(8, lin[idx[0]].n_in, 3100 + j, dev)
-          for j, (name, idx) in enumerate(fused)}
+    fused = syn.fused_linears(syn.LLAMA70B_LINEARS)
+    xs = [decode70b_x(j, dev) for j in range(len(fused))]
     gemvs = []
     t0 = time.perf_counter()
     for layer in range(layers):
-        for name, idx in fused:
-            w = torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama70b_seed(layer, i),
-                                                    0.015, 0, dev) for i in idx])
+        for j in range(len(fused)):
+            w = decode70b_weight(layer, j, dev)
             qw = w4.quantize_pack(w, 128)
             del w
-            gemvs.append((qw, xs[name], torch.empty((8, qw.n_out), dtype=torch.float16, device=dev)))
+            gemvs.append((qw, xs[j], torch.empty((8, qw.n_out), dtype=torch.float16, device=dev)))
     torch.cuda.synchronize()
     log(f"70B stack: {layers} layers quantized in {time.perf_counter() - t0:.1f} s")
-    g = capture(lambda: [w4.gemv(x, qw, y) for qw, x, y in gemvs])
+    g = capture(lambda: [gemv(x, qw, y) for qw, x, y in gemvs])
     el, _ = time_graph(g, 5, 1)
     nbytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 8, 128) for qw, _, _ in gemvs)
     res = dict(layers=layers, m=8, gemvs_per_pass=len(gemvs), ms_per_pass=round(el / 5 * 1e3, 3),
@@ -290,31 +397,19 @@ def bench_decode70b(args, dev):
     return res
 
 
-def student_t_device(n_out, n_in, seed, dev):
-    import torch
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(seed)
-    z = torch.randn((n_out, n_in), generator=gen, device=dev)
-    chi2 = torch.zeros_like(z)
-    for _ in range(3):
-        chi2.addcmul_(e := torch.randn((n_out, n_in), generator=gen, device=dev), e)
-    return z.mul_(torch.rsqrt(chi2.div_(3.0))).mul_(0.02)
-
-
 def bench_single(args, dev):
     """One 4096x4096 linear at m=1 (g=128), cycled over 64 distinct packed copies
     (about 570 MB, beyond the 256 MB Infinity Cache) inside one graph: the
     latency-dominated single-GEMV case."""
     import torch
     import w4a16_dequant_gemv_amd as w4
-    from w4a16_dequant_gemv_amd import synthetic as syn
     n_out = n_in = 4096
-    w = syn.normal_weight_device(n_out, n_in, 1, 0.02, 8, dev)
-    qws = [w4.quantize_pack(w.mul(1.0 + c * 1e-3) if c else w, 128) for c in range(64)]
+    w = single_weight(dev)
+    qws = [w4.quantize_pack(single_copy(w, c), 128) for c in range(SINGLE_COPIES)]
     del w
-    x = syn.activations_f16_device(1, n_in, 101, dev)
+    x = single_x(dev)
     y = torch.empty((1, n_out), dtype=torch.float16, device=dev)
-    gr = capture(lambda: [w4.gemv(x, q, y) for q in qws])
+    gr = capture(lambda: [gemv(x, q, y) for q in qws])
     el, _ = time_graph(gr, 3, 1)
     t = el / (3 * len(qws))
     del qws, gr
@@ -330,44 +425,68 @@ def bench_int8(args, dev):
     import torch
     import w4a16_dequant_gemv_amd as w4
     from w4a16_dequant_gemv_amd import synthetic as syn
-    lin = syn.LLAMA7B_LINEARS
-    fused = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
-    xs = {name: syn.activations_f16_device(1, lin[idx[0]].n_in, 2200 + j, dev)
-          for j, (name, idx) in enumerate(fused)}
+    fused = syn.fused_linears(syn.LLAMA7B_LINEARS)
+    xs = [decode7b_x(j, dev, int8=True) for j in range(len(fused))]
     layers, gemvs = 8, []
     for layer in range(layers):
-        for name, idx in fused:
-            w = torch.cat([syn.normal_weight_device(lin[i].n_out, lin[i].n_in, syn.llama7b_seed(layer, i),
-                                                    0.02, syn.n_outliers(lin[i].n_in), dev) for i in idx])
+        for j in range(len(fused)):
+            w = decode7b_weight(layer, j, dev)
             qw = w4.quantize_pack(w, None, bits=8)
             del w
-            gemvs.append((qw, xs[name], torch.empty((1, qw.n_out), dtype=torch.float16, device=dev)))
-    g = capture(lambda: [w4.gemv(x, qw, y) for qw, x, y in gemvs])
+            gemvs.append((qw, xs[j], torch.empty((1, qw.n_out), dtype=torch.float16, device=dev)))
+    g = capture(lambda: [gemv(x, qw, y) for qw, x, y in gemvs])
     el, _ = time_graph(g, 10, 2)
     nbytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 1, qw.n_in, 8) for qw, _, _ in gemvs)
     res = dict(decode_layers=layers, decode_m=1, decode_group="per-channel",
                decode_gbs=round(nbytes * 10 / el / 1e9, 1),
                decode_us_per_launch=round(el / (10 * len(gemvs)) * 1e6, 2))
     del gemvs, g
-    out, tot_flop, tot_t = [], 0, 0.0
-    for i, pl in enumerate(syn.PREFILL_LINEARS):
-        w = syn.normal_weight_device(pl.n_out, pl.n_in, 4000 + i, 0.02, syn.n_outliers(pl.n_in), dev)
-        qw = w4.quantize_pack(w, 128, bits=8)
-        del w
-        x = syn.activations_f16_device(syn.PREFILL_M, pl.n_in, 4100 + i, dev)
-        y = torch.empty((syn.PREFILL_M, pl.n_out), dtype=torch.float16, device=dev)
-        reps = 20
-        gr = capture(lambda: [w4.gemm(x, qw, y) for _ in range(reps)])
-        settle(gr)
-        el, _ = time_graph(gr, 5, 3)
-        t = el / (5 * reps)
-        flop = 2 * syn.PREFILL_M * pl.n_out * pl.n_in
-        out.append(dict(shape=f"{syn.PREFILL_M}x{pl.n_out}x{pl.n_in}", tflops=round(flop / t / 1e12, 1)))
-        tot_flop += flop
-        tot_t += t
-    res["prefill_g128_shapes"] = out
-    res["prefill_g128_tflops"] = round(tot_flop / tot_t / 1e12, 1)
-    torch.cuda.empty_cache()
+    pre = bench_prefill(args, dev, bits=8)
+    res["prefill_g128_shapes"] = [dict(shape=s["shape"], tflops=s["tflops"]) for s in pre["shapes"]]
+    res["prefill_g128_tflops"] = pre["tflops"]
+    return res
+
+
+def bench_stress_and_quantize(args, dev, host):
+    """Quantizer stress: 8192x28672 Student-t(3) weights with constant and zero
+    groups, for g=128 and g=32 in both modes: quantize+pack and dequant GB/s,
+    then the m=1 GEMV over three packed copies (3 x 125-147 MB, beyond the
+    Infinity Cache)."""
+    import torch
+    import w4a16_dequant_gemv_amd as w4
+    n_out, n_in = STRESS_SHAPE
+    x = stress_x(dev)
+    res = {}
+    for g in (128, 32):
+        w = stress_weight(g, dev)
+        if host is not None:
+            host.setdefault("stress", {})[g] = w[:512].cpu().numpy()
+        for sym in (False, True):
+            mode = "sym" if sym else "asym"
+            qws = [w4.quantize_pack(w, g, sym)]
+            for c in range(1, 3):
+                qws.append(w4.quantize_pack(w.mul(1.0 + c * 1e-3), g, sym))
+            y = torch.empty((1, n_out), dtype=torch.float16, device=dev)
+            reps = 8
+            gr = capture(lambda: [gemv(x, qws[r % 3], y) for r in range(reps * 3)])
+            el, _ = time_graph(gr, 3, 1)
+            t = el / (3 * reps * 3)
+            res[f"gemv_g{g}_{mode}_gbs"] = round(algorithmic_bytes(n_out, n_in, 1, g) / t / 1e9, 1)
+            res[f"gemv_g{g}_{mode}_us"] = round(t * 1e6, 2)
+            del gr
+            qw = qws[0]
+            gq = capture(lambda: [w4.quantize_pack(w, g, sym, out=qw) for _ in range(5)])
+            el, _ = time_graph(gq, 2, 1)
+            res[f"quantize_g{g}_{mode}_gbs"] = round(quantize_bytes(n_out, n_in, g) * 10 / el / 1e9, 1)
+            del gq, qws
+        out = torch.empty_like(w)
+        gd = capture(lambda: [w4.dequant(qw, out) for _ in range(5)])
+        el, _ = time_graph(gd, 2, 1)
+        res[f"dequant_g{g}_gbs"] = round(quantize_bytes(n_out, n_in, g) * 10 / el / 1e9, 1)
+        del w, out, gd, qw
+        torch.cuda.empty_cache()
+    # the keys of the earlier single-mode report
+    res["gemv_g128_gbs"], res["gemv_g32_gbs"] = res["gemv_g128_asym_gbs"], res["gemv_g32_asym_gbs"]
     return res
 
 
@@ -435,13 +554,13 @@ def bench_w8a8(args, dev):
     from w4a16_dequant_gemv_amd import synthetic as syn, w8a8
     out, tot_op, tot_t, tot_layer_t = [], 0, 0.0, 0.0
     for i, lin in enumerate(syn.PREFILL_LINEARS):
-        w = syn.normal_weight_device(lin.n_out, lin.n_in, 4000 + i, 0.02, syn.n_outliers(lin.n_in), dev)
+        w = prefill_weight(i, dev)
         calib = syn.activations_f16_device(512, lin.n_in, 4200 + i, dev)
         act_max = torch.zeros(lin.n_in, dtype=torch.float32, device=dev)
         w8a8.absmax_update(calib, act_max)
         layer = w8a8.W8A8Linear.from_float(w, act_max)
         del w, calib
-        x = syn.activations_f16_device(syn.PREFILL_M, lin.n_in, 4100 + i, dev)
+        x = prefill_x(i, dev)
         qx, sx = w8a8.quantize_act(x, layer.s)
         y = torch.empty((syn.PREFILL_M, lin.n_out), dtype=torch.float16, device=dev)
         reps = 20
@@ -509,38 +628,155 @@ def bench_producers(args, dev):
     return res
 
 
-def bench_stress_and_quantize(args, dev):
-    import torch
-    import w4a16_dequant_gemv_amd as w4
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on bounded samples of each workload.
+# ---------------------------------------------------------------------------
+def cpu_baseline(args, dev, host):
+    """Times the CPU oracle (dequantize, then the binary64 product; the
+    quantizer for quantize+pack) on this host's cores.  Every figure is on the
+    same algorithmic bytes (GB/s) or flops (GFLOP/s) as the GPU figure it is
+    reported beside.  Each leg repeats its sample until `budget` seconds of
+    CPU time have passed (at least once)."""
+    import numpy as np
+    import oracle
     from w4a16_dequant_gemv_amd import synthetic as syn
-    n_out, n_in = 8192, 28672
-    w = student_t_device(n_out, n_in, 5, dev)
-    x = syn.activations_f16_device(1, n_in, 5100, dev)
-    res = {}
-    for g in (128, 32):
-        qws = [w4.quantize_pack(w, g)]
-        for c in range(1, 3):          # three copies (3 x 125-147 MB) to defeat the cache
-            qws.append(w4.quantize_pack(w.mul(1.0 + c * 1e-3), g))
-        y = torch.empty((1, n_out), dtype=torch.float16, device=dev)
-        reps = 8
-        gr = capture(lambda: [w4.gemv(x, qws[r % 3], y) for r in range(reps * 3)])
-        el, _ = time_graph(gr, 3, 1)
-        t = el / (3 * reps * 3)
-        res[f"gemv_g{g}_gbs"] = round(algorithmic_bytes(n_out, n_in, 1, g) / t / 1e9, 1)
-        res[f"gemv_g{g}_us"] = round(t * 1e6, 2)
-        del qws, gr
-    qw = w4.quantize_pack(w, 128)
-    out = torch.empty_like(w)
-    gq = capture(lambda: [w4.quantize_pack(w, 128, out=qw) for _ in range(5)])
-    el, _ = time_graph(gq, 2, 1)
-    qbytes = n_out * n_in * 4 + n_out * n_in // 2 + n_out * (n_in // 128) * 4
-    res["quantize_g128_gbs"] = round(qbytes * 10 / el / 1e9, 1)
-    gd = capture(lambda: [w4.dequant(qw, out) for _ in range(5)])
-    el, _ = time_graph(gd, 2, 1)
-    res["dequant_g128_gbs"] = round(qbytes * 10 / el / 1e9, 1)
-    del w, out
-    torch.cuda.empty_cache()
-    return res
+    orc = oracle.load()
+    budget = args.cpu_seconds / 16.0
+    cores = orc.max_threads()
+
+    def rate(fn, units, share=1.0):
+        t, n = 0.0, 0
+        while t < budget * share or n == 0:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            n += 1
+        return units * n / t, n, t
+
+    legs = {}
+    # config 2: layer 0 of the 7B decode step (fused linears, m = 1)
+    prepared = []
+    for name, w, x in host["decode7b"]:
+        packed, scales, zeros, _ = orc.quantize_pack(w, 128)
+        prepared.append((packed, scales, zeros, x.view(np.uint16), w.shape))
+    step = sum(algorithmic_bytes(s[0], s[1], 1, 128) for *_, s in prepared)
+    gbs, n, t = rate(lambda: [orc.linear_from_packed(x, p, s, z, 128) for p, s, z, x, _ in prepared], step / 1e9,
+                     share=4.0)
+    legs["decode7b_gemv"] = dict(gbs=round(gbs, 3), sample=f"layer 0's four fused GEMVs (m=1) x{n}, {t:.1f} s")
+    # config 1: one 4096x4096 linear, quantize+pack and GEMV, all threads and one
+    w1 = host["single"]
+    gbs, n, t = rate(lambda: orc.quantize_pack(w1, 128), quantize_bytes(4096, 4096, 128) / 1e9)
+    legs["single_quantize"] = dict(gbs=round(gbs, 3), sample=f"4096x4096 g=128 x{n}, {t:.1f} s")
+    p1, s1, z1, _ = orc.quantize_pack(w1, 128)
+    x1 = host["single_x"].view(np.uint16)
+    b1 = algorithmic_bytes(4096, 4096, 1, 128) / 1e9
+    gbs, n, t = rate(lambda: orc.linear_from_packed(x1, p1, s1, z1, 128), b1)
+    legs["single_gemv"] = dict(gbs=round(gbs, 3), sample=f"4096x4096 m=1 x{n}, {t:.1f} s")
+    orc.set_threads(1)
+    try:
+        gbs, n, t = rate(lambda: orc.linear_from_packed(x1, p1, s1, z1, 128), b1)
+    finally:
+        orc.set_threads(cores)
+    legs["single_gemv_1thread"] = dict(gbs=round(gbs, 3), threads=1, sample=f"4096x4096 m=1 x{n}, {t:.1f} s")
+    # config 5: the first 512 rows of the 8192x28672 stress matrix per group size
+    if "stress" in host:
+        xs = host["stress_x"].view(np.uint16)
+        for g, wb in sorted(host["stress"].items()):
+            for sym in (False, True):
+                mode = "sym" if sym else "asym"
+                gbs, n, t = rate(lambda: orc.quantize_pack(wb, g, sym), quantize_bytes(wb.shape[0], wb.shape[1], g) / 1e9)
+                legs[f"stress_quantize_g{g}_{mode}"] = dict(gbs=round(gbs, 3),
+                                                            sample=f"rows 0-511 of 8192x28672 x{n}, {t:.1f} s")
+            pb, sb, zb, _ = orc.quantize_pack(wb, g)
+            gbs, n, t = rate(lambda: orc.linear_from_packed(xs, pb, sb, zb, g),
+                             algorithmic_bytes(wb.shape[0], wb.shape[1], 1, g) / 1e9)
+            legs[f"stress_gemv_g{g}"] = dict(gbs=round(gbs, 3), sample=f"rows 0-511 of 8192x28672, m=1, x{n}, {t:.1f} s")
+    # config 3: 256 sampled rows of each fused linear of layers 0, 40 and 79 at
+    # m = 8, extrapolated to the 80-layer pass by its algorithmic bytes
+    if "decode70b" in host:
+        items = []
+        for layer, j, wr, x in host["decode70b"]:
+            p, s, z, _ = orc.quantize_pack(wr, 128)
+            items.append((p, s, z, x.view(np.uint16), wr.shape))
+        sample_bytes = sum(algorithmic_bytes(sh[0], sh[1], 8, 128) for *_, sh in items)
+        gbs, n, t = rate(lambda: [orc.linear_from_packed(x, p, s, z, 128) for p, s, z, x, _ in items],
+                         sample_bytes / 1e9)
+        pass_bytes = syn.LLAMA70B_LAYERS * sum(algorithmic_bytes(l.n_out, l.n_in, 8, 128)
+                                              for l in syn.fused_linears(syn.LLAMA70B_LINEARS))
+        legs["decode70b_gemv_extrapolated"] = dict(
+            gbs=round(gbs, 3), ms_per_pass_extrapolated=round(pass_bytes / (gbs * 1e9) * 1e3, 1),
+            sample=f"256 rows of each fused linear of layers 0, 40, 79 (m=8) x{n}, {t:.1f} s; "
+                   f"extrapolated to 80 layers")
+    # config 4: 16 rows of x through each prefill shape
+    if "prefill" in host:
+        flop, tt, nn = 0, 0.0, 0
+        for w, x in host["prefill"]:
+            p, s, z, _ = orc.quantize_pack(w, 128)
+            xr = x.view(np.uint16)
+            f = 2 * xr.shape[0] * w.shape[0] * w.shape[1]
+            r, n, t = rate(lambda: orc.linear_from_packed(xr, p, s, z, 128), f / 1e9)
+            flop += f * n
+            tt += t
+            nn += n
+        legs["prefill_gemm"] = dict(gflops=round(flop / tt / 1e9, 3),
+                                    sample=f"16 rows of x (m=2048 workload) through the three 7B shapes, "
+                                           f"{nn} products, {tt:.1f} s")
+    return dict(value=legs["decode7b_gemv"]["gbs"], unit="GB/s", cores=cores, kind="oracle",
+                sample=(f"headline leg: {legs['decode7b_gemv']['sample']} (qkv 12288x4096, o 4096x4096, "
+                        f"gate_up 22016x4096, down 4096x11008; g=128) through the C oracle's dequantize + "
+                        f"binary64 product; the other legs are listed under `legs`"),
+                legs=legs)
+
+
+def host_samples(dev, full):
+    """Host copies of the CPU-baseline samples the GPU legs do not keep (all
+    of them with `full`, else only the single linear's)."""
+    import numpy as np
+    import torch
+    from w4a16_dequant_gemv_amd import synthetic as syn
+    host = {"single": single_weight(dev).cpu().numpy(), "single_x": single_x(dev).cpu().numpy()}
+    if not full:
+        return host
+    host["stress_x"] = stress_x(dev).cpu().numpy()
+    rng = np.random.default_rng(3300)
+    host["decode70b"] = []
+    for layer in (0, 40, 79):
+        for j in range(4):
+            wd = decode70b_weight(layer, j, dev)
+            rows = np.sort(rng.choice(wd.shape[0], size=256, replace=False))
+            host["decode70b"].append((layer, j, wd[torch.from_numpy(rows).to(dev)].cpu().numpy(),
+                                      decode70b_x(j, dev).cpu().numpy()))
+            del wd
+    host["prefill"] = [(prefill_weight(i, dev).cpu().numpy(), prefill_x(i, dev)[:16].cpu().numpy())
+                       for i in range(len(syn.PREFILL_LINEARS))]
+    return host
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 kernel-trace summary.
+# ---------------------------------------------------------------------------
+def trace_summary(path, last, pattern):
+    """Per-kernel statistics of the last `last` dispatches whose kernel name
+    matches `pattern` in a rocprofv3 --kernel-trace CSV (the timed replays of a
+    run come last)."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            if re.search(pattern, name):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+    rows.sort()
+    rows = rows[-last:] if last else rows
+    by = collections.defaultdict(list)
+    for s, e, name in rows:
+        short = re.sub(r"^void |\(.*$|\(anonymous namespace\)::", "", name)
+        by[short].append((e - s) / 1e3)
+    out = {"dispatches": len(rows), "total_us": round(sum(sum(v) for v in by.values()), 2), "kernels": {}}
+    for k, v in sorted(by.items()):
+        out["kernels"][k] = dict(calls=len(v), avg_us=round(sum(v) / len(v), 3), min_us=round(min(v), 3),
+                                 max_us=round(max(v), 3), total_us=round(sum(v), 2))
+    return out
 
 
 def main():
@@ -559,9 +795,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one elementwise copy of 256 MiB (268435456 bytes read and written), "
                          "the known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="CPU time budget of the oracle baseline, shared by its legs")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarize a rocprofv3 kernel trace (no GPU work) and exit")
+    ap.add_argument("--last", type=int, default=0, help="with --trace-summary: only the last N dispatches")
+    ap.add_argument("--kernel", default=r"gemv_|gemm_kernel", help="with --trace-summary: kernel name regex")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary, args.last, args.kernel), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md); use --gpus 1.", file=sys.stderr)
@@ -583,6 +827,7 @@ def main():
         del a, b
     if args.prefill_only:
         pre = bench_prefill(args, dev)
+        check_calls()
         log(f"prefill: {pre}")
         print(json.dumps({
             "metric": "W4A16 prefill GEMM TFLOP/s (m=2048)", "value": pre["tflops"], "unit": "TFLOP/s",
@@ -595,7 +840,8 @@ def main():
     if args.decode_only:
         args.no_extras = True
         args.no_cpu_baseline = True
-    decode, host_w = bench_decode(args, dev)
+    host = None if args.no_cpu_baseline else {}
+    decode = bench_decode(args, dev, host)
     log(f"decode: {decode['gbs']:.1f} GB/s, {decode['ms_per_step']:.3f} ms/step, "
         f"{decode['per_launch_us']:.2f} us per GEMV launch")
     extras = {}
@@ -604,7 +850,7 @@ def main():
         log(f"prefill: {extras['prefill']}")
         extras["decode70b"] = bench_decode70b(args, dev)
         log(f"decode70b: {extras['decode70b']}")
-        extras["stress"] = bench_stress_and_quantize(args, dev)
+        extras["stress"] = bench_stress_and_quantize(args, dev, host)
         log(f"stress: {extras['stress']}")
         extras["single"] = bench_single(args, dev)
         log(f"single 4096x4096 GEMV: {extras['single']}")
@@ -616,13 +862,16 @@ def main():
         log(f"w8a8: {extras['w8a8']}")
         extras["producers"] = bench_producers(args, dev)
         log(f"gptq/awq: {extras['producers']}")
+    check_calls()
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(host_w, args.cpu_seconds)
+    if host is not None:
+        host.update(host_samples(dev, full=not args.no_extras))
+        cpu = cpu_baseline(args, dev, host)
         log(f"cpu baseline: {cpu}")
 
     achieved = decode["bytes_per_launch"] / (decode["per_launch_us"] * 1e-6) / 1e9
     traffic = counters_traffic(decode["bytes_per_launch"])
+    legs = cpu["legs"] if cpu else {}
     record = {
         "metric": "W4A16 decode GEMV HBM GB/s (% peak) + prefill GEMM TFLOPS (% MFMA peak)",
         "value": round(decode["gbs"], 1),
@@ -644,7 +893,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "q4_gemv (gemv_kernel)", "avg_launch_us": round(decode["per_launch_us"], 3),
+                     "kernel": "q4_gemv", "avg_launch_us": round(decode["per_launch_us"], 3),
                      "bytes_per_launch": round(decode["bytes_per_launch"])},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(decode["wall"], 4),
@@ -662,6 +911,21 @@ def main():
         record["kv_codec"] = extras["kv"]
         record["w8a8_smoothquant"] = extras["w8a8"]
         record["gptq_awq"] = extras["producers"]
+        # the oracle's figure beside each GPU figure
+        if legs:
+            record["prefill"]["oracle_gflops"] = legs["prefill_gemm"]["gflops"]
+            record["decode70b"]["oracle_gbs_extrapolated"] = legs["decode70b_gemv_extrapolated"]["gbs"]
+            record["decode70b"]["oracle_ms_per_pass_extrapolated"] = \
+                legs["decode70b_gemv_extrapolated"]["ms_per_pass_extrapolated"]
+            for g in (128, 32):
+                record["stress"][f"oracle_gemv_g{g}_gbs"] = legs[f"stress_gemv_g{g}"]["gbs"]
+                for mode in ("asym", "sym"):
+                    record["stress"][f"oracle_quantize_g{g}_{mode}_gbs"] = legs[f"stress_quantize_g{g}_{mode}"]["gbs"]
+            record["single_gemv_4096x4096"]["oracle_gbs"] = legs["single_gemv"]["gbs"]
+            record["single_gemv_4096x4096"]["oracle_gbs_1thread"] = legs["single_gemv_1thread"]["gbs"]
+            record["single_gemv_4096x4096"]["oracle_quantize_gbs"] = legs["single_quantize"]["gbs"]
+    if legs:
+        record["oracle_decode_gbs"] = legs["decode7b_gemv"]["gbs"]
     print(json.dumps(record), flush=True)
 
 

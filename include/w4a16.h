@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 2
+#define Q4_ABI_VERSION 3
 
 enum {
     Q4_OK = 0,
@@ -180,6 +180,24 @@ int q8_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
 int q8_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
             const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
             int32_t group_size, uint16_t *y, void *stream);
+
+/*
+ * Kernel selection report, for tests and profiling.  Writes to `name` the
+ * kernel instantiation that q4_gemv (op 0) or q4_gemm (op 1) -- q8_gemv and
+ * q8_gemm for bits 8 -- launches for these sizes, in the form profilers
+ * print kernel names (e.g. "gemv_resident_kernel<8, 1, 1, 2, true, 4,
+ * false>"), NUL-terminated and truncated to name_len bytes.  Nothing is
+ * launched and no HIP call is made, so it also works on a host without a
+ * GPU.  The selection can depend on the alignment of the scale and
+ * zero-point arrays, so their addresses are passed: they are inspected,
+ * never dereferenced (any value with the alignment of the real arrays will
+ * do).  Returns the status the linear-layer entry point would return for
+ * these sizes (Q4_ERR_SHAPE also for op or bits outside {0, 1} / {4, 8} or
+ * name_len < 1; Q4_ERR_NULL for a NULL scales, zeros or name).
+ */
+int q4_linear_config(int32_t op, int32_t bits, int64_t m, int64_t n_out, int64_t n_in,
+                     int32_t group_size, const void *scales, const void *zeros,
+                     char *name, int64_t name_len);
 
 #ifdef __cplusplus
 }

@@ -79,7 +79,16 @@ class Oracle:
         lib.orc_awq_loss.argtypes = [_p, _c_i64, _p, _p, _c_i64, _c_i64]
         lib.orc_kv_cache_bytes.restype = ctypes.c_double
         lib.orc_kv_cache_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32]
+        lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+        lib.orc_max_threads.restype = ctypes.c_int
         self.lib = lib
+
+    def set_threads(self, n):
+        """Threads of the oracle's parallel loops (results do not depend on it)."""
+        self.lib.orc_set_num_threads(int(n))
+
+    def max_threads(self):
+        return int(self.lib.orc_max_threads())
 
     # -- binary32 <-> binary16 ------------------------------------------------
     def f32_to_f16(self, a):

@@ -41,9 +41,15 @@
  * Parity status of each function is stated beside it.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Thread count of the parallel loops below (timing of the CPU baseline on
+ * one core and on all of them; results do not depend on it). */
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* binary32 <-> binary16, written from the IEEE 754 definitions.             */

@@ -59,3 +59,21 @@ def assert_bits_equal(got, want, what):
         i = tuple(np.argwhere(neq)[0])
         raise AssertionError(f"{what}: {int(neq.sum())} of {neq.size} differ; first at {i}: "
                              f"gpu={hex(int(got[i]))} oracle={hex(int(want[i]))}")
+
+
+def realign_metadata(qw, align):
+    """The same QuantizedWeight with its scale and zero-point arrays copied to
+    addresses congruent to `align` modulo 16 (fresh allocations are 256-byte
+    aligned; the prefill kernel picks its metadata loads by alignment)."""
+    from w4a16_dequant_gemv_amd.api import QuantizedWeight
+    off = (align % 16) // 2
+    if off == 0:
+        return qw
+
+    def moved(t):
+        buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+        v = buf[off:off + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v
+    return QuantizedWeight(qw.qweight, moved(qw.scales), moved(qw.zeros), qw.n_out, qw.n_in,
+                           qw.group_size, qw.symmetric, qw.bits)

@@ -11,12 +11,12 @@ can be imported on machines without the library.
 """
 import importlib
 
-__all__ = ["quantize_pack", "dequant", "gemv", "gemm", "linear", "QuantizedWeight",
+__all__ = ["quantize_pack", "dequant", "gemv", "gemm", "linear", "kernel_config", "QuantizedWeight",
            "W4A16Error", "synthetic", "kv", "w8a8", "producers"]
 
 
 def __getattr__(name):
-    if name in ("quantize_pack", "dequant", "gemv", "gemm", "linear",
+    if name in ("quantize_pack", "dequant", "gemv", "gemm", "linear", "kernel_config",
                 "QuantizedWeight", "W4A16Error"):
         api = importlib.import_module(".api", __name__)
         return getattr(api, name)

@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libw4a16.so")
 
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_GROUP, Q4_ERR_ALIGN, Q4_ERR_HIP = range(6)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol the public header declares, with its ctypes signature.
 _p = ctypes.c_void_p
@@ -25,6 +25,7 @@ SIGNATURES = {
     "q8_dequant": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p]),
     "q8_gemv": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
     "q8_gemm": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
+    "q4_linear_config": (ctypes.c_int, [_i32, _i32, _i64, _i64, _i64, _i32, _p, _p, ctypes.c_char_p, _i64]),
     "kv_quant_tokens": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p]),
     "kv_quant_channels": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p]),
     "kv_dequant_tokens": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p]),

@@ -156,6 +156,23 @@ def gemm(x, qw, out=None):
     return _linear("gemm", x, qw, out)
 
 
+def kernel_config(kind, bits, m, n_out, n_in, group_size, scales_ptr=256, zeros_ptr=256):
+    """Name of the kernel instantiation gemv (kind "gemv") or gemm (kind
+    "gemm") launches for these sizes, as profilers print it.  Nothing is
+    launched; works without a GPU.  The selection can depend on the alignment
+    of the scale and zero-point arrays: pass their data_ptr() values (the
+    default, 256, stands for freshly allocated arrays)."""
+    import ctypes
+    if kind not in ("gemv", "gemm"):
+        raise W4A16Error(f"kind must be 'gemv' or 'gemm', got {kind!r}")
+    if group_size is None:
+        group_size = n_in
+    buf = ctypes.create_string_buffer(128)
+    check(lib().q4_linear_config(0 if kind == "gemv" else 1, bits, m, n_out, n_in, group_size,
+                                 scales_ptr, zeros_ptr, buf, len(buf)), "q4_linear_config")
+    return buf.value.decode()
+
+
 def linear(x, qw, out=None):
     """y = x W'^T, routed to the GEMV kernels for m <= 16 and the GEMM otherwise."""
     return gemv(x, qw, out) if x.shape[0] <= MAX_GEMV_ROWS else gemm(x, qw, out)

@@ -216,6 +216,30 @@ int q8_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                                  (hipStream_t)stream));
 }
 
+int q4_linear_config(int32_t op, int32_t bits, int64_t m, int64_t n_out, int64_t n_in, int32_t group_size,
+                     const void *scales, const void *zeros, char *name, int64_t name_len)
+{
+    if (!scales || !zeros || !name) return Q4_ERR_NULL;
+    if ((op != 0 && op != 1) || (bits != 4 && bits != 8) || name_len < 1) return Q4_ERR_SHAPE;
+    if (int rc = check_weight_shape(n_out, n_in, group_size)) return rc;
+    const int64_t max_m = op == 0 ? 16 : kMaxRows;
+    if (m <= 0 || m > max_m || m * n_in > kMaxElems || m * n_out > kMaxElems) return Q4_ERR_SHAPE;
+    if (!aligned(scales, 2) || !aligned(zeros, 2)) return Q4_ERR_ALIGN;
+    // only the two addresses are inspected (for their alignment); nothing is
+    // dereferenced and no HIP call is made
+    const uint16_t *s = static_cast<const uint16_t *>(scales), *z = static_cast<const uint16_t *>(zeros);
+    const char *cfg = nullptr;
+    const hipError_t e = op == 0 ? q4_launch_gemv(nullptr, nullptr, s, z, m, n_out, n_in, group_size, bits, nullptr,
+                                                  nullptr, &cfg)
+                                 : q4_launch_gemm(nullptr, nullptr, s, z, m, n_out, n_in, group_size, bits, nullptr,
+                                                  nullptr, &cfg);
+    if (e != hipSuccess || !cfg) return finish(e == hipSuccess ? hipErrorInvalidValue : e);
+    int64_t i = 0;
+    for (; i + 1 < name_len && cfg[i]; ++i) name[i] = cfg[i];
+    name[i] = '\0';
+    return Q4_OK;
+}
+
 int kv_quant_tokens(const uint16_t *x, int64_t rows, int32_t d, int32_t bits, int8_t *q, float *scale,
                     void *stream)
 {

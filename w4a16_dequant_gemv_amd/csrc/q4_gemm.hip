@@ -52,6 +52,7 @@
 // output-column inside a band, so an XCD's range covers few row tiles of x
 // (BM rows x n_in fp16 each, the larger operand) and many column tiles of
 // the packed weights (BN rows x n_in/2 bytes each), which its L2 shares.
+#include <string>
 #include <type_traits>
 
 #include "gemm_tile.h"
@@ -527,8 +528,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 template <int BM, int BN, int BITS, bool PAIR_SZ, int SZV = 1>
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                        const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
-                       uint16_t *y, hipStream_t stream)
+                       uint16_t *y, hipStream_t stream, const char **query)
 {
+    if (query) {
+        // the kernel's name in the form profilers print it
+        static const std::string s = "gemm_kernel<" + std::to_string(BM) + ", " + std::to_string(BN) + ", " +
+                                     std::to_string(BITS) + ", " + (PAIR_SZ ? "true" : "false") + ", " +
+                                     std::to_string(SZV) + ">";
+        *query = s.c_str();
+        return hipSuccess;
+    }
     const int tiles_m = (m + BM - 1) / BM, tiles_n = (n_out + BN - 1) / BN;
     const size_t lds = kStages * (size_t)(BM + BN) * 128;
     // steps per run of SZV groups: SZV << (group_shift - 6), a power of two
@@ -550,22 +559,22 @@ hipError_t launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_
 template <int BITS>
 hipError_t launch_paired(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                          const uint16_t *zeros, int m, int n_out, int n_in, int shift, uint16_t *y,
-                         hipStream_t stream)
+                         hipStream_t stream, const char **query)
 {
     const int groups = shift >= 31 ? 1 : n_in >> shift;
     const uintptr_t a = reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros);
     if (shift >= 6 && shift <= 8 && groups % 8 == 0 && (a & 15) == 0)
-        return launch_gemm<256, 128, BITS, true, 8>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream);
+        return launch_gemm<256, 128, BITS, true, 8>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream, query);
     if (shift >= 6 && shift <= 8 && groups % 2 == 0 && (a & 3) == 0)
-        return launch_gemm<256, 128, BITS, true, 2>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream);
-    return launch_gemm<256, 128, BITS, true>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream);
+        return launch_gemm<256, 128, BITS, true, 2>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream, query);
+    return launch_gemm<256, 128, BITS, true>(x, qweight, scales, zeros, m, n_out, n_in, shift, y, stream, query);
 }
 
 }  // namespace
 
 hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, int bits, uint16_t *y, hipStream_t stream)
+                          int group_size, int bits, uint16_t *y, hipStream_t stream, const char **query)
 {
     // group k of a row is k >> shift; a per-channel group of any other
     // length than a power of two uses shift 31 (every k in group 0)
@@ -573,11 +582,11 @@ hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint
     while ((1 << shift) < group_size) ++shift;
     if ((1 << shift) != group_size) shift = 31;
     if (bits == 8)
-        return launch_paired<8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
+        return launch_paired<8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream, query);
     // INT4 slices hold 32 codes: with groups of 32 the two slices of a row
     // step belong to different groups
     if (group_size == 32)
         return launch_gemm<256, 128, 4, false>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y,
-                                               stream);
-    return launch_paired<4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
+                                               stream, query);
+    return launch_paired<4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream, query);
 }

@@ -68,6 +68,8 @@
 // re-reading weights, so no load is conditional and the compiler keeps the
 // ring in flight.  Partial results of the SPLIT waves are summed in LDS in a
 // fixed order, so results are deterministic.
+#include <string>
+
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -708,6 +710,26 @@ Geometry make_geometry(int m, int n_out, int n_in, int group_shift, int bits)
     return g;
 }
 
+// Kernel names in the form profilers print them, for the configuration query.
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS, bool PAIRED>
+const char *resident_name()
+{
+    static const std::string s = "gemv_resident_kernel<" + std::to_string(SPLIT) + ", " + std::to_string(CT) +
+                                 ", " + std::to_string(UNROLL) + ", " + std::to_string(DEPTH) + ", " +
+                                 (FOLD ? "true" : "false") + ", " + std::to_string(BITS) + ", " +
+                                 (PAIRED ? "true" : "false") + ">";
+    return s.c_str();
+}
+
+template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX, int BITS>
+const char *window_name()
+{
+    static const std::string s = "gemv_window_kernel<" + std::to_string(SPLIT) + ", " + std::to_string(CT) + ", " +
+                                 std::to_string(UNROLL) + ", " + (FOLD ? "true" : "false") + ", " +
+                                 std::to_string(MMAX) + ", " + std::to_string(BITS) + ">";
+    return s.c_str();
+}
+
 template <typename K>
 hipError_t allow_full_lds(K kernel)
 {
@@ -721,7 +743,7 @@ hipError_t allow_full_lds(K kernel)
 template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4, bool PAIRED = false>
 bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                    const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
-                   uint16_t *y, hipStream_t stream, hipError_t *err)
+                   uint16_t *y, hipStream_t stream, const char **query, hipError_t *err)
 {
     static_assert(SPLIT >= CT || SPLIT == 1, "the LDS reduction assigns one wave per tile");
     Geometry g = make_geometry(m, n_out, n_in, group_shift, BITS);
@@ -733,6 +755,11 @@ bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *s
     const size_t part = SPLIT > 1 ? (size_t)SPLIT * CT * 1024 : 0;
     const size_t lds = (x_bytes > part ? x_bytes : part) + (size_t)16 * CT * g.sz_stride * 4;
     if (lds > kMaxLds) return false;
+    *err = hipSuccess;
+    if (query) {
+        *query = resident_name<SPLIT, CT, UNROLL, DEPTH, FOLD, BITS, PAIRED>();
+        return true;
+    }
     auto kernel = gemv_resident_kernel<SPLIT, CT, UNROLL, DEPTH, FOLD, BITS, PAIRED>;
     if (lds > 64 * 1024) {
         const hipError_t e = allow_full_lds(kernel);
@@ -751,7 +778,7 @@ bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *s
 template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX, int BITS = 4>
 bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                  const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
-                 uint16_t *y, hipStream_t stream, hipError_t *err)
+                 uint16_t *y, hipStream_t stream, const char **query, hipError_t *err)
 {
     static_assert(SPLIT >= CT || SPLIT == 1, "the LDS reduction assigns one wave per tile");
     static_assert(SPLIT * UNROLL % 2 == 0, "a window must hold whole groups of 256");
@@ -764,6 +791,11 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
     const size_t part = SPLIT > 1 ? (size_t)SPLIT * CT * 1024 : 0;
     const size_t lds = (x_region > part ? x_region : part) + 2 * (size_t)16 * CT * g.sz_stride * 4;
     if (lds > kMaxLds) return false;
+    *err = hipSuccess;
+    if (query) {
+        *query = window_name<SPLIT, CT, UNROLL, FOLD, MMAX, BITS>();
+        return true;
+    }
     auto kernel = gemv_window_kernel<SPLIT, CT, UNROLL, FOLD, MMAX, BITS>;
     if (lds > 64 * 1024) {
         const hipError_t e = allow_full_lds(kernel);
@@ -791,17 +823,17 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 template <bool FOLD, int BITS>
 hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
-                    uint16_t *y, hipStream_t stream)
+                    uint16_t *y, hipStream_t stream, const char **query)
 {
     hipError_t e = hipSuccess;
     const int kblocks = (n_in + 127) >> 7;
     const int tiles = (n_out + 15) / 16;
 #define Q4_RES(S, C, U, D) \
-    if (plan_resident<S, C, U, D, FOLD, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+    if (plan_resident<S, C, U, D, FOLD, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e
 #define Q4_PAIR(S, C, U, D) \
-    if (plan_resident<S, C, U, D, FOLD, BITS, true>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+    if (plan_resident<S, C, U, D, FOLD, BITS, true>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e
 #define Q4_WIN(S, C, U, MM) \
-    if (plan_window<S, C, U, FOLD, MM, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, &e)) return e
+    if (plan_window<S, C, U, FOLD, MM, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e
     if (kblocks >= 16) {
         if constexpr (BITS == 8) {
             // twice the bytes per code: fewer waves per tile keep more
@@ -850,7 +882,7 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
 
 hipError_t q4_launch_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, int bits, uint16_t *y, hipStream_t stream)
+                          int group_size, int bits, uint16_t *y, hipStream_t stream, const char **query)
 {
     // group k of a row is k >> shift; a per-channel group of any other
     // length than a power of two uses shift 31 (every k in group 0)
@@ -858,13 +890,13 @@ hipError_t q4_launch_gemv(const uint16_t *x, const uint32_t *qweight, const uint
     while ((1 << shift) < group_size) ++shift;
     if ((1 << shift) != group_size) shift = 31;
     if (bits == 8)
-        return dispatch<false, 8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
+        return dispatch<false, 8>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream, query);
     // The fold applies s and z once per 128-wide block after summing raw
     // codes, subtracting z * sum(x) from the code sum; with one scale per
     // row (per-channel) most codes sit at z and that subtraction would
     // cancel terms far larger than the result, so per-channel weights take
     // the exact-subtraction form.
     return (group_size == 128 || group_size == 256)
-               ? dispatch<true, 4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream)
-               : dispatch<false, 4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream);
+               ? dispatch<true, 4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream, query)
+               : dispatch<false, 4>(x, qweight, scales, zeros, (int)m, (int)n_out, (int)n_in, shift, y, stream, query);
 }

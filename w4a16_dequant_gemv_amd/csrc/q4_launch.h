@@ -13,13 +13,19 @@ hipError_t q4_launch_dequant(const uint32_t *qweight, const uint16_t *scales,
                              const uint16_t *zeros, int64_t n_out, int64_t n_in,
                              int group_size, int bits, float *out, hipStream_t stream);
 
+// With `query` non-null the linear-layer launchers launch nothing and make
+// no HIP call: *query is set to the name of the kernel instantiation the
+// dispatch rules select for these arguments (x and y are not read; only the
+// addresses of scales and zeros are inspected, for their alignment).
 hipError_t q4_launch_gemv(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, int bits, uint16_t *y, hipStream_t stream);
+                          int group_size, int bits, uint16_t *y, hipStream_t stream,
+                          const char **query = nullptr);
 
 hipError_t q4_launch_gemm(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                           const uint16_t *zeros, int64_t m, int64_t n_out, int64_t n_in,
-                          int group_size, int bits, uint16_t *y, hipStream_t stream);
+                          int group_size, int bits, uint16_t *y, hipStream_t stream,
+                          const char **query = nullptr);
 
 // KV-cache codec (kv_codec.hip); 8 <= d <= 512, d % 8 == 0, bits 4 or 8,
 // per-channel blocks of t tokens with ceil(t / (2048 / d)) <= 32.

@@ -81,6 +81,34 @@ def normal_weight_device(n_out, n_in, seed, std, n_outlier_cols, device):
     return w
 
 
+def student_t_weight_device(n_out, n_in, seed, group_size, device, nu=3, scale=0.02,
+                            const_frac=0.01, zero_frac=0.001):
+    """float32 [n_out][n_in] = scale * t(nu) on the GPU (t drawn as
+    N(0,1) / sqrt(chi2(nu) / nu), nu an integer); a `const_frac` share of the
+    groups of `group_size` is set to the group's first value and a
+    `zero_frac` share to exactly 0 (group indices drawn on the host)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    w = torch.randn((n_out, n_in), generator=gen, device=device, dtype=torch.float32)
+    chi2 = torch.zeros_like(w)
+    for _ in range(nu):
+        e = torch.randn((n_out, n_in), generator=gen, device=device, dtype=torch.float32)
+        chi2.addcmul_(e, e)
+        del e
+    w.mul_(torch.rsqrt(chi2.div_(float(nu)))).mul_(scale)
+    del chi2
+    groups = w.view(n_out * (n_in // group_size), group_size)
+    total = groups.shape[0]
+    n_const = int(round(const_frac * total))
+    n_zero = int(round(zero_frac * total))
+    pick = torch.from_numpy(_rng(seed).choice(total, size=n_const + n_zero, replace=False)).to(device)
+    const_rows = pick[:n_const]
+    groups[const_rows] = groups[const_rows, :1].expand(-1, group_size)
+    groups[pick[n_const:]] = 0.0
+    return w
+
+
 def activations_f16_device(m, n_in, seed, device):
     import torch
     gen = torch.Generator(device=device)
@@ -134,6 +162,18 @@ LLAMA70B_LAYERS = 80
 PREFILL_M = 2048
 PREFILL_LINEARS = (Linear("qkvo", 4096, 4096), Linear("gate_up", 11008, 4096),
                    Linear("down", 4096, 11008))
+
+
+# Serving engines store q, k and v as one matrix and gate and up as another:
+# a decode step then runs four dependent linear layers per decoder layer
+# (quantization is per row, so this equals quantizing each linear alone).
+FUSED_LAYOUT = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+
+
+def fused_linears(linears):
+    """The four fused linears of a layer, in decode order."""
+    return tuple(Linear(name, sum(linears[i].n_out for i in idx), linears[idx[0]].n_in)
+                 for name, idx in FUSED_LAYOUT)
 
 
 def llama7b_seed(layer, index):
