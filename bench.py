@@ -755,6 +755,12 @@ def host_samples(dev, full):
 # ---------------------------------------------------------------------------
 # rocprofv3 kernel-trace summary.
 # ---------------------------------------------------------------------------
+def kernel_short_name(name):
+    """'void (anonymous namespace)::k<1, 2>(int, ...)' -> 'k<1, 2>'."""
+    name = re.sub(r"^void |\(anonymous namespace\)::", "", name)
+    return re.sub(r"\(.*$", "", name)
+
+
 def trace_summary(path, last, pattern):
     """Per-kernel statistics of the last `last` dispatches whose kernel name
     matches `pattern` in a rocprofv3 --kernel-trace CSV (the timed replays of a
@@ -770,12 +776,38 @@ def trace_summary(path, last, pattern):
     rows = rows[-last:] if last else rows
     by = collections.defaultdict(list)
     for s, e, name in rows:
-        short = re.sub(r"^void |\(.*$|\(anonymous namespace\)::", "", name)
+        short = kernel_short_name(name)
         by[short].append((e - s) / 1e3)
     out = {"dispatches": len(rows), "total_us": round(sum(sum(v) for v in by.values()), 2), "kernels": {}}
     for k, v in sorted(by.items()):
         out["kernels"][k] = dict(calls=len(v), avg_us=round(sum(v) / len(v), 3), min_us=round(min(v), 3),
                                  max_us=round(max(v), 3), total_us=round(sum(v), 2))
+    return out
+
+
+def counter_summary(path, pattern):
+    """Mean of each counter per (kernel, grid size) over the dispatches whose
+    kernel name matches `pattern` in a rocprofv3 --pmc CSV."""
+    import csv
+    acc = collections.defaultdict(lambda: [0.0, 0])
+    dur = collections.defaultdict(list)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if not re.search(pattern, name):
+                continue
+            short = kernel_short_name(name)
+            key = (short, int(r["Grid_Size"]))
+            a = acc[key + (r["Counter_Name"],)]
+            a[0] += float(r["Counter_Value"])
+            a[1] += 1
+            dur[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for (short, grid, counter), (tot, n) in sorted(acc.items()):
+        d = out.setdefault(f"{short} grid={grid}", {})
+        d[counter] = round(tot / n, 1)
+        d["dispatches"] = n
+        d["avg_us"] = round(sum(dur[(short, grid)]) / len(dur[(short, grid)]) / 1e3, 2)
     return out
 
 
@@ -799,10 +831,16 @@ def main():
                     help="CPU time budget of the oracle baseline, shared by its legs")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarize a rocprofv3 kernel trace (no GPU work) and exit")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="mean of each counter per kernel and grid size in a rocprofv3 --pmc CSV, and exit")
     ap.add_argument("--last", type=int, default=0, help="with --trace-summary: only the last N dispatches")
-    ap.add_argument("--kernel", default=r"gemv_|gemm_kernel", help="with --trace-summary: kernel name regex")
+    ap.add_argument("--kernel", default=r"gemv_|gemm_kernel",
+                    help="with --trace-summary / --counter-summary: kernel name regex")
     args = ap.parse_args()
 
+    if args.counter_summary:
+        print(json.dumps(counter_summary(args.counter_summary, args.kernel), indent=1))
+        return
     if args.trace_summary:
         print(json.dumps(trace_summary(args.trace_summary, args.last, args.kernel), indent=1))
         return
