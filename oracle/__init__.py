@@ -402,10 +402,13 @@ _DEFAULT = None
 
 
 def load():
-    """The oracle built from oracle/q4_oracle.c (built with gcc if absent)."""
+    """The oracle built from oracle/q4_oracle.c (built with gcc if absent), or
+    the build named by the ORACLE_LIB environment variable (the sanitizer
+    check loads an ASan/UBSan build that way)."""
     global _DEFAULT
     if _DEFAULT is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        _DEFAULT = Oracle(_build.LIB)
+        _DEFAULT = Oracle(path)
     return _DEFAULT

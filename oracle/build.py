@@ -23,5 +23,21 @@ def build(src=SRC, out=LIB, extra_flags=()):
     return out
 
 
+# AddressSanitizer + UndefinedBehaviorSanitizer build, with the ROCm clang so
+# that it shares one sanitizer runtime with the HIP library's host code.
+CLANG = "/opt/rocm/llvm/bin/clang"
+SAN_FLAGS = ["-O1", "-g", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+             "-fopenmp", "-Wall", "-Wextra", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(out, src=SRC):
+    """Compile `src` into `out` with ASan and UBSan (CPU checking of the oracle)."""
+    tmp = out + ".tmp"
+    subprocess.run([CLANG, *SAN_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())

@@ -4,7 +4,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libw4a16.so")
+# W4A16_LIB names another build of the same sources (the host-sanitizer
+# check uses it); there is no other implementation to fall back on.
+LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(PKG, "libw4a16.so")
 
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_GROUP, Q4_ERR_ALIGN, Q4_ERR_HIP = range(6)
 ABI_VERSION = 3

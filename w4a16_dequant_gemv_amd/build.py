@@ -37,9 +37,16 @@ SOURCES = ["q4_api.hip", "q4_quantize.hip", "q4_gemv.hip", "q4_gemm.hip", "kv_co
            "producers.hip"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (argument checking,
+# dispatch, launch code); the device code is compiled as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+
+
+def _compile(src, build_dir=BUILD_DIR, extra=()):
+    obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 target feature; that
     # warning is expected and dropped here.
@@ -63,6 +70,17 @@ def build(verbose=True):
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_host_sanitized(out, build_dir):
+    """libw4a16 with ASan/UBSan on its host code, linked to `out` (objects in
+    `build_dir`); load it with the clang ASan runtime preloaded."""
+    os.makedirs(build_dir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, build_dir, HOST_SANITIZE), SOURCES))
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                    "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", out, *objs], check=True)
+    return out
 
 
 if __name__ == "__main__":
