@@ -70,6 +70,27 @@ int gptq_quantize(const float *w, const float *u, int64_t n_out, int64_t n, int3
                   int32_t bits, int32_t symmetric, void *workspace, int64_t workspace_bytes,
                   uint32_t *qweight, uint16_t *scales, uint16_t *zeros, void *stream);
 
+/*
+ * gptq_quantize without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid allocation).  Same arguments and
+ * results as gptq_quantize (bit for bit); the working copy of W and the
+ * block errors live in a scratch array of gptq_quantize_noalloc_max_bytes()
+ * bytes (72 MiB) that the library holds on every GPU it runs on until the
+ * process ends.  A problem with gptq_quantize_workspace_size(n_out, n) above
+ * that size returns Q4_ERR_CAPACITY before any HIP call (n_out x n = 4096 x
+ * 4096 fits).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialized by the caller.  The scratch needs no clearing: each call writes
+ * every part of it before reading it.
+ */
+int gptq_quantize_noalloc(const float *w, const float *u, int64_t n_out, int64_t n, int32_t group_size,
+                          int32_t bits, int32_t symmetric, uint32_t *qweight, uint16_t *scales,
+                          uint16_t *zeros, void *stream);
+
+/* Size in bytes of gptq_quantize_noalloc's scratch on each GPU. */
+int64_t gptq_quantize_noalloc_max_bytes(void);
+
 /* Workspace bytes of awq_quantize. */
 int64_t awq_workspace_size(int64_t n_out, int64_t n, int64_t tokens, int32_t n_grid, int32_t group_size);
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 3
+#define Q4_ABI_VERSION 4
 
 enum {
     Q4_OK = 0,
@@ -63,8 +63,10 @@ enum {
                           n_in (per-channel with n_in a multiple of 32) */
     Q4_ERR_ALIGN = 4,  /* w, w_out, qweight or x not 16-byte aligned, or an
                           fp16 array not 2-byte aligned */
-    Q4_ERR_HIP = 5     /* the HIP runtime refused the launch; see
+    Q4_ERR_HIP = 5,    /* the HIP runtime refused the launch; see
                           q4_last_hip_error() */
+    Q4_ERR_CAPACITY = 6 /* a no-allocation entry point was given a problem
+                           larger than its fixed scratch memory */
 };
 
 /* Largest sizes accepted: n_in <= 2^20, n_out <= 2^24, m <= 2^24, and

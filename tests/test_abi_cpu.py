@@ -272,6 +272,12 @@ def test_producers_reject(L):
     assert L.gptq_quantize(P16, P16, 8, 256, 128, 3, 0, P16, ws, P16, P2, P2, None) == _lib.Q4_ERR_SHAPE
     assert L.gptq_quantize(P16, P16, 8, 256, 128, 4, 0, P16, ws - 1, P16, P2, P2, None) == _lib.Q4_ERR_SHAPE
     assert L.gptq_quantize(P16, P16, 8, 256, 128, 4, 0, P16, ws, P16 + 4, P2, P2, None) == _lib.Q4_ERR_ALIGN
+    # the no-allocation column loop: the same checks, and its fixed capacity
+    assert L.gptq_quantize_noalloc(P16, P16, 8, 256, 48, 4, 0, P16, P2, P2, None) == _lib.Q4_ERR_GROUP
+    assert L.gptq_quantize_noalloc(P16, None, 8, 256, 128, 4, 0, P16, P2, P2, None) == _lib.Q4_ERR_NULL
+    assert L.gptq_quantize_noalloc(P16 + 4, P16, 8, 256, 128, 4, 0, P16, P2, P2, None) == _lib.Q4_ERR_ALIGN
+    assert L.gptq_quantize_workspace_size(4096, 4096) <= L.gptq_quantize_noalloc_max_bytes() == 72 << 20
+    assert L.gptq_quantize_noalloc(P16, P16, 4096, 4608, 128, 4, 0, P16, P2, P2, None) == _lib.Q4_ERR_CAPACITY
     wa = L.awq_workspace_size(8, 256, 64, 20, 128)
     assert wa > 0
     assert L.awq_quantize(P16, P16, 64, 8, 256, 128, 4, 0, 0, P16, wa, P16, P2, P2, P16, None, None, None) == _lib.Q4_ERR_SHAPE

@@ -8,8 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # check uses it); there is no other implementation to fall back on.
 LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(PKG, "libw4a16.so")
 
-Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_GROUP, Q4_ERR_ALIGN, Q4_ERR_HIP = range(6)
-ABI_VERSION = 3
+Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_GROUP, Q4_ERR_ALIGN, Q4_ERR_HIP, Q4_ERR_CAPACITY = range(7)
+ABI_VERSION = 4
 
 # Every symbol the public header declares, with its ctypes signature.
 _p = ctypes.c_void_p
@@ -43,6 +43,8 @@ SIGNATURES = {
     "gptq_hinv_factor": (ctypes.c_int, [_p, _i64, _i64, ctypes.c_double, _p, _i64, _p, _p]),
     "gptq_quantize_workspace_size": (_i64, [_i64, _i64]),
     "gptq_quantize": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
+    "gptq_quantize_noalloc": (ctypes.c_int, [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),
+    "gptq_quantize_noalloc_max_bytes": (_i64, []),
     "awq_workspace_size": (_i64, [_i64, _i64, _i64, _i32, _i32]),
     "awq_quantize": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _i64, _p, _p, _p, _p,
                                     _p, _p, _p]),

@@ -28,6 +28,8 @@
 //     updates give the same values as immediate ones;
 //   * AWQ's losses: each output error sums over k in order in binary64, then
 //     over tokens, then over output channels, in order.
+#include <mutex>
+
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -519,4 +521,43 @@ hipError_t awq_launch(const float *w, const uint16_t *x, int64_t t, int64_t n_ou
         if (e != hipSuccess) return e;
     }
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation GPTQ column loop: a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: each device's copy is looked up once with
+// hipGetSymbolAddress and that pointer is what the launches receive.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kGptqNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t gptq_noalloc_scratch(hipStream_t stream, void **ptr)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
 }

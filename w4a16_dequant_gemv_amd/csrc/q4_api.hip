@@ -113,6 +113,8 @@ const char *q4_strerror(int status)
     case Q4_ERR_ALIGN: return "misaligned pointer: w, w_out, qweight and x need 16 bytes, fp16 "
                               "arrays 2 bytes";
     case Q4_ERR_HIP: return "the HIP runtime refused the launch (see q4_last_hip_error)";
+    case Q4_ERR_CAPACITY: return "the problem needs more scratch memory than the no-allocation entry point "
+                                 "holds (see gptq_quantize_noalloc_max_bytes)";
     default: return "unknown status";
     }
 }
@@ -355,6 +357,23 @@ int64_t gptq_quantize_workspace_size(int64_t n_out, int64_t n)
 {
     return (n_out > 0 && n > 0) ? gptq_loop_workspace(n_out, n) : 0;
 }
+
+int gptq_quantize_noalloc(const float *w, const float *u, int64_t n_out, int64_t n, int32_t group_size,
+                          int32_t bits, int32_t symmetric, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
+                          void *stream)
+{
+    if (!w || !u || !qweight || !scales || !zeros) return Q4_ERR_NULL;
+    if (int rc = check_producer(n_out, n, group_size, bits)) return rc;
+    if (gptq_loop_workspace(n_out, n) > kGptqNoAllocScratchBytes) return Q4_ERR_CAPACITY;
+    if (!aligned(w, 16) || !aligned(u, 4) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+        return Q4_ERR_ALIGN;
+    void *ws = nullptr;
+    if (hipError_t e = gptq_noalloc_scratch((hipStream_t)stream, &ws)) return finish(e);
+    return finish(gptq_launch_loop(w, u, n_out, (int)n, group_size, bits, symmetric != 0, ws, qweight, scales, zeros,
+                                   (hipStream_t)stream));
+}
+
+int64_t gptq_quantize_noalloc_max_bytes(void) { return kGptqNoAllocScratchBytes; }
 
 int64_t awq_workspace_size(int64_t n_out, int64_t n, int64_t tokens, int32_t n_grid, int32_t group_size)
 {

@@ -62,6 +62,10 @@ hipError_t gptq_launch_factor(const uint16_t *x, int64_t t, int n, double damp, 
 hipError_t gptq_launch_loop(const float *w, const float *u, int64_t n_out, int n, int group_size, int bits,
                             bool symmetric, void *workspace, uint32_t *qweight, uint16_t *scales, uint16_t *zeros,
                             hipStream_t stream);
+// The no-allocation GPTQ column loop's scratch: its size, and this
+// stream's device copy of it (looked up once per device).
+constexpr int64_t kGptqNoAllocScratchBytes = int64_t(72) << 20;
+hipError_t gptq_noalloc_scratch(hipStream_t stream, void **ptr);
 hipError_t awq_launch(const float *w, const uint16_t *x, int64_t t, int64_t n_out, int n, int group_size, int bits,
                       bool symmetric, int n_grid, void *workspace, uint32_t *qweight, uint16_t *scales,
                       uint16_t *zeros, float *s_out, int32_t *best_out, float *losses_out, hipStream_t stream);

@@ -61,6 +61,24 @@ def gptq_quantize(w, u, group_size=128, bits=4, symmetric=False):
     return qw
 
 
+def gptq_quantize_noalloc(w, u, group_size=128, bits=4, symmetric=False, out=None):
+    """gptq_quantize through the entry point that allocates nothing on the
+    device (its scratch is the library's own fixed array); pass `out` (a
+    QuantizedWeight) to make the call allocation-free on the torch side too."""
+    _dev(w, torch.float32, "w")
+    n_out, n = w.shape
+    _need(u, torch.float32, (n, n), "u")
+    _same_device(w, u)
+    if group_size is None:
+        group_size = n
+    qw = out if out is not None else _outputs(n_out, n, group_size, bits, symmetric, w.device)
+    with torch.cuda.device(w.device):
+        check(lib().gptq_quantize_noalloc(w.data_ptr(), u.data_ptr(), n_out, n, group_size, bits,
+                                          int(bool(symmetric)), qw.qweight.data_ptr(), qw.scales.data_ptr(),
+                                          qw.zeros.data_ptr(), _stream(w)), "gptq_quantize_noalloc")
+    return qw
+
+
 def gptq(w, x, group_size=128, bits=4, symmetric=False, damp=0.01):
     """GPTQ of W [n_out, n] on calibration tokens x [tokens, n] -> QuantizedWeight."""
     return gptq_quantize(w, gptq_factor(x, damp), group_size, bits, symmetric)
