@@ -17,8 +17,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # Sizes around every threshold of the rules: tile counts (16 channels per
 # tile) of 1, 2, 256, 257, 512, 640, 768, 769 and beyond; 128-wide k blocks
 # below 16, 16..63, 64..127 and 128 or more, with and without a partial last
-# block; x that fits the LDS-resident kernels or not at every m.
-N_IN = [32, 96, 128, 1024, 2016, 2048, 2080, 4096, 4224, 8192, 8320, 11008, 16384, 16416, 28672,
+# block; rows of 1 to 8 chunks of 2048 codes and more; x that fits the
+# LDS-resident kernels or not at every m; metadata 16- and 2-byte aligned.
+N_IN = [32, 96, 128, 1024, 2016, 2048, 2080, 4096, 4224, 8192, 8320, 11008, 13312, 16384, 16416, 28672,
         32768, 65536, 131072, 262144, 1048576]
 N_OUT = [16, 17, 100, 4096, 4112, 8192, 10240, 12288, 12304, 22016, 28672, 57344, 131072]
 GROUPS = (32, 64, 128, 256, None)
@@ -46,7 +47,8 @@ def reachable():
                         if n_out * n_in > 2 ** 34:
                             continue
                         for m in (range(1, 17) if kind == "gemv" else (17, 300, 2048)):
-                            for align in ((256,) if kind == "gemv" else (256, 260, 258)):
+                            aligns = ((256, 258) if m == 1 else (256,)) if kind == "gemv" else (256, 260, 258)
+                            for align in aligns:
                                 c = Case(kind, bits, m, n_out, n_in, gs, align)
                                 try:
                                     name = config(c)
@@ -86,7 +88,8 @@ def test_bench_configurations_have_parity_cases(covered):
 def test_profiled_kernels_are_covered(covered):
     """Every q4_gemv / q4_gemm instantiation named in a committed profile
     summary is one the parity tests run (a stale profile fails here)."""
-    pat = re.compile(r"\b(gemv_resident_kernel|gemv_window_kernel|gemv_stream_kernel|gemm_kernel)<[^<>]*>")
+    pat = re.compile(r"\b(gemv_resident_kernel|gemv_window_kernel|gemv_rowstream_kernel|gemv_persistent_kernel|"
+                     r"gemv_stream_kernel|gemm_kernel)<[^<>]*>")
     seen = set()
     for path in glob.glob(os.path.join(ROOT, "profiles", "*")):
         with open(path, encoding="utf-8") as f:

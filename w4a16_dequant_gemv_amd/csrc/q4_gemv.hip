@@ -6,12 +6,15 @@
 // weight byte is read once per call and the arithmetic intensity is a few
 // FLOP per byte, so the kernel is bound by HBM bandwidth.
 //
-// What limits it on gfx950 is how many weight bytes each CU keeps in flight,
-// not arithmetic.  Per-lane gathers of x, scales and zero-points cost as many
-// vector-memory issue slots as the 1-KiB weight loads themselves, so x
-// (pre-permuted into MFMA fragment order) and the scale|zero pairs of the
-// workgroup's rows are staged cooperatively in LDS and read back with
-// ds_read, and each wave issues one global load per 1 KiB of weights.
+// What limits it on gfx950 is how many weight bytes each CU keeps in flight
+// and how many instructions each KiB of weights costs a wave, not FLOPs.
+// Per-lane gathers of x, scales and zero-points cost as many vector-memory
+// issue slots as the 1-KiB weight loads themselves, so x (pre-permuted) and
+// the scale|zero pairs of the workgroup's rows are staged cooperatively in
+// LDS and read back with ds_read, and each wave issues one global load per
+// 1 KiB of weights.  For one row of x (m = 1) the row-streaming kernel below
+// drops the matrix cores altogether: it spends fewer instructions per KiB
+// than any MFMA mapping, whose 16-wide tiles are mostly padding there.
 //
 // Matrix-core mapping.  v_mfma_f32_16x16x32_f16 multiplies a 16x32 A block
 // (rows = the m rows of x, padded to 16 with copies of row m-1 whose results
@@ -64,12 +67,16 @@
 //  * windowed: for larger m * n_in, x and scale|zero pairs are staged one
 //    window (one stage of blocks) ahead in double-buffered LDS, with one
 //    barrier per window.
+// and, for m = 1 with grouped INT4 rows of up to 16384 codes, the
+// row-streaming kernel (one wave per row, VALU dot products), described
+// where it is defined.
 // Loads past the last block are redirected to x (hot in L2) rather than
 // re-reading weights, so no load is conditional and the compiler keeps the
 // ring in flight.  Partial results of the SPLIT waves are summed in LDS in a
 // fixed order, so results are deterministic.
 #include <string>
 
+#include "gemm_tile.h"
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -544,6 +551,186 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Row-streaming kernel (m = 1, INT4, groups of 32 to 256, n_in <= 16384).
+//
+// Every load instruction of a wave reads one contiguous KiB of one row (2048
+// codes; lane l holds codes 32l .. 32l + 31 of the chunk), the access pattern
+// HBM serves fastest, and a wave streams RW whole rows.  With one row of x
+// the matrix cores would waste fifteen sixteenths of their work, so the
+// products run on the VALU as v_dot2_f32_f16: masking a packed word with
+// 0x000F000F leaves the codes (c_t, c_{t+4}) as the fp16 subnormals c 2^-24
+// (with 0x00F000F0, four bits up: c 2^-20), exact, and the lane's x slice is
+// permuted once into the matching pairs (x_t, x_{t+4}).  A lane's 32 codes
+// lie in one group (groups have at least 32 codes), so its scale and
+// zero-point are applied once, in fp32:
+//   y += s 2^24 (A + B / 16 - z X24),
+// A and B the dot products of the c 2^-24 and c 2^-20 codes, X24 = 2^-24
+// times the sum of the lane's 32 x.  x, pre-permuted, and the sums X24 are
+// staged once per workgroup in LDS, 80 bytes per 64-byte lane slot (the
+// padding keeps the 16-byte reads of neighbouring lanes on distinct banks),
+// with the workgroup's scale and zero-point rows beside them.  A row's
+// partial sums are added across the wave with DPP row rotations and the
+// gfx950 permlane swaps, all on the VALU.
+// ---------------------------------------------------------------------------
+constexpr int kRsSlot = 80;          // LDS bytes per lane slot of x (64 + padding)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return bitcast<float>(__builtin_amdgcn_mov_dpp(bitcast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// The sum of v over the 64 lanes, in every lane.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp_f32<0x128>(v);          // row_ror:8
+    v += dpp_f32<0x124>(v);          // row_ror:4
+    v += dpp_f32<0x4E>(v);           // quad_perm [2,3,0,1]
+    v += dpp_f32<0xB1>(v);           // quad_perm [1,0,3,2]
+    const auto a = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(v), bitcast<uint32_t>(v), false, false);
+    v = bitcast<float>(a[0]) + bitcast<float>(a[1]);          // rows 0+1, 2+3
+    const auto b = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(v), bitcast<uint32_t>(v), false, false);
+    return bitcast<float>(b[0]) + bitcast<float>(b[1]);       // halves
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(bitcast<f16x2>(a), bitcast<f16x2>(b), c, false);
+}
+
+// 16 bytes at offset o of a scale or zero-point run of `bytes` bytes (even).
+// A vector that straddles the end is read as halves, each wholly inside or
+// wholly past the run; past it a buffer load reads 0.
+__device__ __forceinline__ u32x4 meta_vec(__amdgpu_buffer_rsrc_t r, int o, int bytes)
+{
+    if (o + 16 <= bytes || o >= bytes) return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, o + 4 * i, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, o + 4 * i + 2, 0, 0);
+        v[i] = lo | (hi << 16);
+    }
+    return v;
+}
+
+template <int NC, int RW, int W>
+__global__ __launch_bounds__(64 * W) void gemv_rowstream_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    uint16_t *__restrict__ y, Geometry geo)
+{
+    constexpr int R = W * RW;             // rows per workgroup
+    constexpr int L = RW * NC;            // loads per wave
+    constexpr int THREADS = 64 * W;
+    constexpr int XP = NC * 256;          // 16-byte pieces of x (past n_in they read as 0)
+    constexpr int XI = (XP + THREADS - 1) / THREADS;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+
+    const int n_out = geo.n_out, n_in = geo.n_in, G = geo.groups_per_row, gshift = geo.group_shift;
+    char *x_lds = lds;                                                    // [NC * 64][kRsSlot]
+    float *xs_lds = reinterpret_cast<float *>(lds + NC * 64 * kRsSlot);   // [NC * 64]
+    uint16_t *s_lds = reinterpret_cast<uint16_t *>(xs_lds + NC * 64);     // [R][G]
+    uint16_t *z_lds = s_lds + ((R * G + 7) & ~7);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg_row0 = blockIdx.x * R, row0 = wg_row0 + wave * RW;
+    const int row_bytes = n_in / 2;
+
+    // staging loads: this workgroup's scale and zero-point rows (bytes past
+    // the last row read as 0) and x, issued before the weights
+    const int meta = min(R, n_out - wg_row0) * G * 2;
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(scales + (int64_t)wg_row0 * G), (short)0, meta, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(zeros + (int64_t)wg_row0 * G), (short)0, meta, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x), (short)0, n_in * 2, kBufferFlags);
+    const int n_vec = (R * G * 2 + 15) >> 4;
+    const u32x4 sv = meta_vec(sr, tid * 16, meta);
+    const u32x4 zv = meta_vec(zr, tid * 16, meta);
+    u32x4 xv[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (tid + i * THREADS) * 16, 0, 0);
+
+    // the weights: load i is chunk i % NC of row row0 + i / NC.  Rows past
+    // n_out read the last row, and lanes past the end of a row its last 16
+    // bytes (their x is 0); neither is ever stored.
+    const char *wbase = reinterpret_cast<const char *>(qweight);
+    u32x4 ring[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int r = min(row0 + i / NC, n_out - 1);
+        const uint32_t off = min((uint32_t)(1024 * (i % NC) + 16 * lane), (uint32_t)row_bytes - 16u);
+        ring[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wbase + (int64_t)r * row_bytes + off));
+    }
+
+    if (tid < n_vec) {
+        reinterpret_cast<u32x4 *>(s_lds)[tid] = sv;
+        reinterpret_cast<u32x4 *>(z_lds)[tid] = zv;
+    }
+    for (int v = tid + THREADS; v < n_vec; v += THREADS) {
+        reinterpret_cast<u32x4 *>(s_lds)[v] = meta_vec(sr, v * 16, meta);
+        reinterpret_cast<u32x4 *>(z_lds)[v] = meta_vec(zr, v * 16, meta);
+    }
+    // piece p holds x[8p .. 8p + 7]; slot p / 4 is (chunk, lane); the four
+    // threads of a slot are neighbouring lanes, so a quad sum gives X24
+    const uint32_t ones = 0x3C003C00u;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int p = tid + i * THREADS;
+        const u32x4 pp = bitcast<u32x4>(pair_order(xv[i]));
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t = dot2_f16(pp[e], ones, t);
+        t += dpp_f32<0xB1>(t);
+        t += dpp_f32<0x4E>(t);
+        if (p < XP) {
+            *reinterpret_cast<u32x4 *>(x_lds + (p >> 2) * kRsSlot + (p & 3) * 16) = pp;
+            if ((p & 3) == 0) xs_lds[p >> 2] = t * 5.9604644775390625e-08f;     // 2^-24
+        }
+    }
+    barrier_keep_vmem();
+
+    u32x4 xp[NC][4];
+    float x24[NC];
+#pragma unroll
+    for (int h = 0; h < NC; ++h) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xp[h][j] = *reinterpret_cast<const u32x4 *>(x_lds + (h * 64 + lane) * kRsSlot + 16 * j);
+        x24[h] = xs_lds[h * 64 + lane];
+    }
+    float acc[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int r = i / NC, h = i % NC;
+        const u32x4 w = ring[i];
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t v = w[j], v8 = v >> 8;
+            a = dot2_f16(v & 0x000F000Fu, xp[h][j][0], a);      // codes 8j, 8j+4 as c 2^-24
+            b = dot2_f16(v & 0x00F000F0u, xp[h][j][1], b);      // codes 8j+1, 8j+5 as c 2^-20
+            a = dot2_f16(v8 & 0x000F000Fu, xp[h][j][2], a);     // 8j+2, 8j+6
+            b = dot2_f16(v8 & 0x00F000F0u, xp[h][j][3], b);     // 8j+3, 8j+7
+        }
+        const int e = (wave * RW + r) * G + min((2048 * h + 32 * lane) >> gshift, G - 1);
+        const float s = half_bits_to_float(s_lds[e]) * 16777216.0f;     // s 2^24, exact
+        const float z = half_bits_to_float(z_lds[e]);
+        acc[r] = __builtin_fmaf(s, __builtin_fmaf(-z, x24[h], __builtin_fmaf(b, 0.0625f, a)), acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const float t = wave_sum(acc[r]);
+        if (lane == r && row0 + r < n_out) y[row0 + r] = bitcast<uint16_t>((_Float16)t);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Windowed kernel: x and scale|zero pairs staged one window ahead.
 // ---------------------------------------------------------------------------
 template <int XC, int SC>
@@ -775,6 +962,41 @@ bool plan_resident(const uint16_t *x, const uint32_t *qweight, const uint16_t *s
     return true;
 }
 
+template <int NC, int RW, int W>
+bool plan_rowstream(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                    const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
+                    uint16_t *y, hipStream_t stream, const char **query, hipError_t *err)
+{
+    static_assert(RW == 1 || RW == 2 || RW == 4 || RW == 8, "one storing lane per row");
+    // m = 1, groups of 32 to 256 codes, NC chunks of 2048 codes per row, and
+    // scale and zero-point arrays the staging reads as 4-byte words
+    if (m != 1 || group_shift < 5 || group_shift > 8 || (n_in & 31) != 0 || (n_in + 2047) / 2048 != NC)
+        return false;
+    if (((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 3) != 0) return false;
+    Geometry g = make_geometry(m, n_out, n_in, group_shift, 4);
+    constexpr int R = W * RW;
+    const size_t lds = (size_t)NC * 64 * (kRsSlot + 4) + 2 * (size_t)((R * g.groups_per_row + 7) & ~7) * 2;
+    if (lds > kMaxLds) return false;
+    *err = hipSuccess;
+    if (query) {
+        static const std::string name = "gemv_rowstream_kernel<" + std::to_string(NC) + ", " + std::to_string(RW) +
+                                        ", " + std::to_string(W) + ">";
+        *query = name.c_str();
+        return true;
+    }
+    auto kernel = gemv_rowstream_kernel<NC, RW, W>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = allow_full_lds(kernel);
+        if (e != hipSuccess) {
+            *err = e;
+            return true;
+        }
+    }
+    kernel<<<dim3((unsigned)((n_out + R - 1) / R)), dim3(64 * W), lds, stream>>>(x, qweight, scales, zeros, y, g);
+    *err = hipGetLastError();
+    return true;
+}
+
 template <int SPLIT, int CT, int UNROLL, bool FOLD, int MMAX, int BITS = 4>
 bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
                  const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
@@ -813,7 +1035,10 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 
 // Configurations chosen from measured sweeps on MI355X over the decode
 // shapes (7B and 70B projections, m = 1 and 8, INT4 and INT8); other shapes
-// fall through to the nearest rule.  Paired INT4 loads pay on rows of 8192
+// fall through to the nearest rule.  One row of x with grouped INT4 weights
+// takes the row-streaming kernel (14-31 % faster than the MFMA kernels on
+// every such shape swept, 4096 to 16384 codes per row) unless the scale or
+// zero-point array is only 2-byte aligned or rows are longer than 16384.  Paired INT4 loads pay on rows of 8192
 // codes and more (9-26 % on the 70B and 8192x28672 shapes); on the
 // 4096-wide 7B linears, whose launches are short and dependent, they
 // measured the same as the fragment-order loads, which are kept there.
@@ -834,6 +1059,20 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
     if (plan_resident<S, C, U, D, FOLD, BITS, true>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e
 #define Q4_WIN(S, C, U, MM) \
     if (plan_window<S, C, U, FOLD, MM, BITS>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e
+#define Q4_RS(NC) \
+    case NC: \
+        if (plan_rowstream<NC, 1, 8>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e; \
+        break
+    if constexpr (BITS == 4) {
+        // one token, grouped INT4 rows of up to 16384 codes: one wave per row
+        // (8 rows per workgroup measured best on every such shape swept)
+        if (m == 1) {
+            switch ((n_in + 2047) / 2048) {
+                Q4_RS(1); Q4_RS(2); Q4_RS(3); Q4_RS(4); Q4_RS(5); Q4_RS(6); Q4_RS(7); Q4_RS(8);
+            default: break;
+            }
+        }
+    }
     if (kblocks >= 16) {
         if constexpr (BITS == 8) {
             // twice the bytes per code: fewer waves per tile keep more
@@ -875,6 +1114,7 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
 #undef Q4_RES
 #undef Q4_PAIR
 #undef Q4_WIN
+#undef Q4_RS
     return hipErrorInvalidValue;                // unreachable: the last window always fits
 }
 
