@@ -59,6 +59,8 @@ COVERAGE = [Case(*c) for c in (
     ("gemv", 4, 1, 12301, 8320, 128, 256),     # gemv_rowstream_kernel<5, 1, 8> (ragged rows, odd group count, partial chunk)
     ("gemv", 4, 1, 1000, 13312, 32, 256),      # gemv_rowstream_kernel<7, 1, 8> (partial last chunk of 2048)
     ("gemv", 4, 1, 8192, 16384, 128, 256),     # gemv_rowstream_kernel<8, 1, 8>
+    ("gemv", 4, 3, 32777, 2048, 128, 256),     # gemv_persistent_kernel<8, 4, 2, 1, true, true> (ragged last group)
+    ("gemv", 4, 8, 32800, 4096, 256, 256),     # gemv_persistent_kernel<8, 4, 2, 1, true, true> (groups of 256)
     ("gemv", 4, 4, 17, 16416, 32, 256),        # gemv_window_kernel<16, 2, 1, false, 8, 4>
     ("gemv", 8, 4, 17, 16416, 32, 256),        # gemv_window_kernel<16, 2, 1, false, 8, 8>
     ("gemv", 4, 5, 17, 16384, 128, 256),       # gemv_window_kernel<16, 2, 1, true, 8, 4>

@@ -74,6 +74,7 @@
 // re-reading weights, so no load is conditional and the compiler keeps the
 // ring in flight.  Partial results of the SPLIT waves are summed in LDS in a
 // fixed order, so results are deterministic.
+#include <atomic>
 #include <string>
 
 #include "gemm_tile.h"
@@ -89,6 +90,7 @@ struct Geometry {
     int sz_stride;          // u32 per LDS row of scale|zero pairs (odd)
     int x_row_bytes;        // LDS bytes per row of x (padded)
     int sz_vector;          // scale/zero arrays allow 16-byte loads
+    int groups;             // tile groups (persistent kernel)
 };
 
 // Per-lane weight registers of one stage: UNROLL blocks x CT tiles x the
@@ -731,6 +733,309 @@ __global__ __launch_bounds__(64 * W) void gemv_rowstream_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Persistent kernel (INT4, 2 <= m <= 8): a workgroup stages x once and then
+// walks the tile groups blockIdx.x, blockIdx.x + gridDim.x, ...  The weight
+// ring runs on across group boundaries (the last stages of a group load the
+// first stages of the next), so HBM stays busy while a group's partial sums
+// are reduced and stored and the next group's scale|zero pairs are staged.
+// The pairs and the partial sums share one LDS region; only quarters 0 and 1
+// of the MFMA output (rows 0..7) are kept, since m <= 8.
+// ---------------------------------------------------------------------------
+template <int CT, bool PAIRED>
+struct GroupLoads {
+    struct Group {
+        const char *base;            // the group's first row
+        uint32_t off[CT][2];         // byte offset of this lane's rows (clamped to the matrix)
+        bool live;                   // false: past the last group, loads go to x
+    };
+    const char *qweight, *xsafe;
+    uint32_t row_bytes, last;        // last: final 16-byte slot of a row
+    uint32_t lanepart[2];            // this lane's bytes within a block (paired: a 128-byte run)
+    int lrow[CT][2];                 // this lane's rows within a group, unclamped
+    int kblocks, last_full_quarter, quarter;
+
+    __device__ __forceinline__ void init(const uint32_t *qw, const uint16_t *x, const Geometry &geo, int col, int q)
+    {
+        qweight = reinterpret_cast<const char *>(qw);
+        xsafe = reinterpret_cast<const char *>(x);
+        row_bytes = (uint32_t)geo.words_per_row * 4u;
+        last = row_bytes - 16u;
+        kblocks = geo.kblocks;
+        last_full_quarter = geo.last_full_quarter;
+        quarter = q;
+        const bool low = col < 8;
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            lrow[t][0] = t * 16 + (PAIRED ? (col & 7) : col);
+            lrow[t][1] = t * 16 + 8 + (col & 7);
+        }
+        if (PAIRED) {
+            lanepart[0] = low ? 16u * (uint32_t)q : 64u + 16u * (uint32_t)q;
+            lanepart[1] = low ? 64u + 16u * (uint32_t)q : 16u * (uint32_t)q;
+        } else {
+            lanepart[0] = lanepart[1] = 16u * (uint32_t)q;
+        }
+    }
+    __device__ __forceinline__ void set(Group &g, int row0, int n_out, bool live) const
+    {
+        g.live = live;
+        g.base = qweight + (int64_t)(live ? row0 : 0) * row_bytes;
+        const int lim = live ? n_out - 1 - row0 : 0;
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) g.off[t][h] = (uint32_t)min(lrow[t][h], lim) * row_bytes;
+    }
+    // Load h of unit u of tile t: paired, u is a 128-byte run (blocks 2u and
+    // 2u+1); otherwise u is a 128-code block and h is 0.  Past the end (or a
+    // dead group) the load reads x instead.
+    __device__ __forceinline__ u32x4 load(const char *base, const uint32_t (&off)[CT][2], bool live, int u, int t,
+                                          int h) const
+    {
+        uint32_t o;
+        bool inside;
+        if (PAIRED) {
+            inside = live && 2 * u < kblocks;
+            o = off[t][h] + min((uint32_t)u * 128u + lanepart[h], last);
+        } else {
+            // a padding quarter of a partial last block reads the last whole slice
+            const int qs = (u == kblocks - 1 && quarter > last_full_quarter) ? last_full_quarter - quarter : 0;
+            inside = live && u < kblocks;
+            o = off[t][0] + lanepart[0] + (uint32_t)(u * 64 + qs * 16);
+        }
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>((inside ? base : xsafe) + (inside ? o : 0u)));
+    }
+};
+
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, bool PAIRED>
+__global__ __launch_bounds__(64 * SPLIT) void gemv_persistent_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    uint16_t *__restrict__ y, Geometry geo)
+{
+    constexpr int THREADS = 64 * SPLIT;
+    constexpr int ROWS = 16 * CT;
+    constexpr int SB = SPLIT * UNROLL;
+    static_assert(!PAIRED || UNROLL % 2 == 0, "paired loads cover two blocks");
+    static_assert(SPLIT >= CT || SPLIT == 1, "the LDS reduction assigns one wave per tile");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+
+    const int m = geo.m, n_out = geo.n_out, n_in = geo.n_in, gshift = geo.group_shift;
+    const int kblocks = geo.kblocks, G = geo.groups_per_row, ngroups = geo.groups;
+    const int x_bytes = m * geo.x_row_bytes;
+    char *x_lds = lds;
+    uint32_t *sz_lds = reinterpret_cast<uint32_t *>(lds + x_bytes);
+    f32x4 *part = reinterpret_cast<f32x4 *>(lds + x_bytes);     // [SPLIT][CT][32], after the pairs are read
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int quarter = lane >> 4;
+    const int nstages = (kblocks + SB - 1) / SB;
+
+    using GL = GroupLoads<CT, PAIRED>;
+    GL gl;
+    gl.init(qweight, x, geo, col, quarter);
+    typename GL::Group cur, nxt;
+    int tg = blockIdx.x;
+    int ntg = tg + (int)gridDim.x;
+    gl.set(cur, tg * ROWS, n_out, true);
+    gl.set(nxt, ntg * ROWS, n_out, ntg < ngroups);
+
+    // Stage i of the current group; i >= nstages is stage i - nstages of the next.
+    auto load_stage = [&](Stage<CT, UNROLL, 4> &st, int i) {
+        const bool in_cur = i < nstages;
+        const int ii = in_cur ? i : i - nstages;
+        const char *base = in_cur ? cur.base : nxt.base;
+        const bool live = in_cur ? cur.live : nxt.live;
+        uint32_t off[CT][2];
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) off[t][h] = in_cur ? cur.off[t][h] : nxt.off[t][h];
+        if constexpr (PAIRED) {
+#pragma unroll
+            for (int v = 0; v < UNROLL / 2; ++v)
+#pragma unroll
+                for (int t = 0; t < CT; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        st.w[2 * v + h][t] = gl.load(base, off, live, (ii * SPLIT + wave) * (UNROLL / 2) + v, t, h);
+        } else {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int t = 0; t < CT; ++t) st.w[u][t] = gl.load(base, off, live, (ii * SPLIT + wave) * UNROLL + u, t, 0);
+        }
+    };
+
+    // ---- x, staged once (chunk c = (row, block, quarter) holds 32 values)
+    const int n_chunks = m * kblocks * 4;
+    auto x_load = [&](int c, u32x4 v[4]) {
+        c = min(c, n_chunks - 1);
+        const int r = c / (kblocks * 4), rem = c % (kblocks * 4);
+        const int k = min(rem * 32, n_in - 32);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (int64_t)r * n_in + k);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = src[j];
+    };
+    auto x_store = [&](int c, const u32x4 v[4]) {
+        if (c < n_chunks) {
+            const int r = c / (kblocks * 4), rem = c % (kblocks * 4);
+            store_x_chunk<4>(x_lds + r * geo.x_row_bytes + (rem >> 2) * 256, rem & 3, v);
+        }
+    };
+    // ---- scale|zero pairs of the group starting at row `row0`
+    const int n_items = ROWS * G;
+    auto sz_vec = [&](int row0) { return geo.sz_vector && row0 + ROWS <= n_out; };
+    auto sz_units = [&](int row0) { return sz_vec(row0) ? n_items / 8 : n_items; };
+    auto sz_load = [&](int row0, int c, u32x4 &s8, u32x4 &z8) {
+        if (sz_vec(row0)) {
+            c = min(c, n_items / 8 - 1);
+            s8 = reinterpret_cast<const u32x4 *>(scales + (int64_t)row0 * G)[c];
+            z8 = reinterpret_cast<const u32x4 *>(zeros + (int64_t)row0 * G)[c];
+        } else {
+            c = min(c, n_items - 1);
+            const int r = c / G, g = c - r * G;
+            const int64_t off = (int64_t)min(row0 + r, n_out - 1) * G + g;
+            s8 = u32x4{(uint32_t)scales[off], 0u, 0u, 0u};
+            z8 = u32x4{(uint32_t)zeros[off], 0u, 0u, 0u};
+        }
+    };
+    auto sz_store = [&](int row0, int c, const u32x4 &s8, const u32x4 &z8) {
+        if (sz_vec(row0)) {
+            if (c < n_items / 8) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = c * 8 + i, r = e / G, g = e - r * G;
+                    const uint32_t sh = (s8[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    const uint32_t zh = (z8[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    sz_lds[r * geo.sz_stride + g] = sh | (zh << 16);
+                }
+            }
+        } else if (c < n_items) {
+            const int r = c / G, g = c - r * G;
+            sz_lds[r * geo.sz_stride + g] = s8[0] | (z8[0] << 16);
+        }
+    };
+
+    int row0 = tg * ROWS;
+    u32x4 xv[4], s8, z8;
+    x_load(tid, xv);
+    sz_load(row0, tid, s8, z8);
+    Stage<CT, UNROLL, 4> ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_stage(ring[d], d);
+    x_store(tid, xv);
+    sz_store(row0, tid, s8, z8);
+    for (int c = tid + THREADS; c < n_chunks; c += THREADS) {
+        x_load(c, xv);
+        x_store(c, xv);
+    }
+    for (int c = tid + THREADS; c < sz_units(row0); c += THREADS) {
+        sz_load(row0, c, s8, z8);
+        sz_store(row0, c, s8, z8);
+    }
+    __syncthreads();
+
+    const char *xrow = x_lds + min(col, m - 1) * geo.x_row_bytes;
+    const uint32_t *szrow = sz_lds + col * geo.sz_stride;
+    for (;;) {
+        f32x4 acc[CT];
+#pragma unroll
+        for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](const Stage<CT, UNROLL, 4> &st, int i) {
+            Stage<CT, UNROLL, 4> up;
+            if constexpr (PAIRED) {
+#pragma unroll
+                for (int v = 0; v < UNROLL / 2; ++v)
+#pragma unroll
+                    for (int t = 0; t < CT; ++t)
+                        unpair(st.w[2 * v][t], st.w[2 * v + 1][t], col < 8, up.w[2 * v][t], up.w[2 * v + 1][t]);
+            }
+            const Stage<CT, UNROLL, 4> &frag = PAIRED ? up : st;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int kb = (i * SPLIT + wave) * UNROLL + u;
+                const int kbc = min(kb, kblocks - 1);
+                f16x8 a[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    a[t] = *reinterpret_cast<const f16x8 *>(xrow + kbc * 256 + t * 64 + quarter * 16);
+                const int qe = (kbc == kblocks - 1) ? min(quarter, geo.last_full_quarter) : quarter;
+                const int g = ((kbc << 7) + (qe << 5)) >> gshift;
+                uint32_t sz[CT];
+#pragma unroll
+                for (int t = 0; t < CT; ++t) sz[t] = szrow[t * 16 * geo.sz_stride + g];
+                const bool valid = kb < kblocks && !(kb == kblocks - 1 && quarter > geo.last_full_quarter);
+                process_block<CT, FOLD, 4>(acc, a, frag.w[u], sz, valid);
+            }
+        };
+        for (int i0 = 0; i0 < nstages; i0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int i = i0 + d;
+                if (i < nstages) compute(ring[d], i);
+                load_stage(ring[d], i + DEPTH);
+            }
+        }
+        // nstages is a multiple of DEPTH (the planner checks it), so slot d
+        // now holds stage d of the next group
+        const bool has_next = ntg < ngroups;
+        const int nrow0 = ntg * ROWS;
+        if (has_next) sz_load(nrow0, tid, s8, z8);
+        __syncthreads();                                  // every wave is done with the pairs
+        const int col_n = row0 + col;
+        if (SPLIT > 1) {
+            if (lane < 32) {
+#pragma unroll
+                for (int t = 0; t < CT; ++t) part[(wave * CT + t) * 32 + lane] = acc[t];
+            }
+            __syncthreads();
+            if (wave < CT && lane < 32) {
+                const int t = wave;
+                f32x4 sum = part[t * 32 + lane];
+#pragma unroll
+                for (int w = 1; w < SPLIT; ++w) sum += part[(w * CT + t) * 32 + lane];
+                const int n = col_n + t * 16;
+                if (n < n_out) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 4 * quarter + r;
+                        if (row < m) y[(int64_t)row * n_out + n] = bitcast<uint16_t>((_Float16)sum[r]);
+                    }
+                }
+            }
+        } else if (lane < 32) {
+#pragma unroll
+            for (int t = 0; t < CT; ++t) {
+                const int n = col_n + t * 16;
+                if (n >= n_out) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * quarter + r;
+                    if (row < m) y[(int64_t)row * n_out + n] = bitcast<uint16_t>((_Float16)acc[t][r]);
+                }
+            }
+        }
+        if (!has_next) break;
+        __syncthreads();                                  // the partial sums have been read
+        sz_store(nrow0, tid, s8, z8);
+        for (int c = tid + THREADS; c < sz_units(nrow0); c += THREADS) {
+            sz_load(nrow0, c, s8, z8);
+            sz_store(nrow0, c, s8, z8);
+        }
+        __syncthreads();
+        tg = ntg;
+        row0 = nrow0;
+        ntg = tg + (int)gridDim.x;
+        cur = nxt;
+        gl.set(nxt, ntg * ROWS, n_out, ntg < ngroups);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Windowed kernel: x and scale|zero pairs staged one window ahead.
 // ---------------------------------------------------------------------------
 template <int XC, int SC>
@@ -894,6 +1199,7 @@ Geometry make_geometry(int m, int n_out, int n_in, int group_shift, int bits)
     g.sz_stride = 0;
     g.x_row_bytes = 0;
     g.sz_vector = 0;
+    g.groups = 0;
     return g;
 }
 
@@ -993,6 +1299,86 @@ bool plan_rowstream(const uint16_t *x, const uint32_t *qweight, const uint16_t *
         }
     }
     kernel<<<dim3((unsigned)((n_out + R - 1) / R)), dim3(64 * W), lds, stream>>>(x, qweight, scales, zeros, y, g);
+    *err = hipGetLastError();
+    return true;
+}
+
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, bool PAIRED>
+const char *persistent_name()
+{
+    static const std::string s = "gemv_persistent_kernel<" + std::to_string(SPLIT) + ", " + std::to_string(CT) +
+                                 ", " + std::to_string(UNROLL) + ", " + std::to_string(DEPTH) + ", " +
+                                 (FOLD ? "true" : "false") + ", " + (PAIRED ? "true" : "false") + ">";
+    return s.c_str();
+}
+
+// Compute units of the current device (looked up once per device).
+hipError_t device_cus(int *cus)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    *cus = v;
+    return hipSuccess;
+}
+
+template <int SPLIT, int CT, int UNROLL, int DEPTH, bool FOLD, int BITS = 4, bool PAIRED = false>
+bool plan_persistent(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
+                     uint16_t *y, hipStream_t stream, const char **query, hipError_t *err)
+{
+    static_assert(BITS == 4, "INT4 only");
+    if (m > 8) return false;
+    Geometry g = make_geometry(m, n_out, n_in, group_shift, BITS);
+    constexpr int SB = SPLIT * UNROLL;
+    const int nstages = (g.kblocks + SB - 1) / SB;
+    if (nstages % DEPTH != 0) return false;
+    g.sz_stride = g.groups_per_row | 1;
+    g.x_row_bytes = g.kblocks * 256 + 16;
+    g.sz_vector = ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 15) == 0 &&
+                  (16 * CT * g.groups_per_row) % 8 == 0;
+    const int tiles = (n_out + 15) / 16;
+    g.groups = (tiles + CT - 1) / CT;
+    const size_t x_bytes = (size_t)m * g.x_row_bytes;
+    const size_t sz = (size_t)16 * CT * g.sz_stride * 4, part = (size_t)SPLIT * CT * 512;
+    const size_t lds = x_bytes + (sz > part ? sz : part);
+    if (lds > kMaxLds) return false;
+    *err = hipSuccess;
+    if (query) {
+        *query = persistent_name<SPLIT, CT, UNROLL, DEPTH, FOLD, PAIRED>();
+        return true;
+    }
+    auto kernel = gemv_persistent_kernel<SPLIT, CT, UNROLL, DEPTH, FOLD, PAIRED>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = allow_full_lds(kernel);
+        if (e != hipSuccess) {
+            *err = e;
+            return true;
+        }
+    }
+    // one workgroup per slot the device can hold at once: each then walks
+    // its share of the tile groups
+    int cus = 0, per_cu = 0;
+    hipError_t e = device_cus(&cus);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel), 64 * SPLIT,
+                                                         lds);
+    if (e != hipSuccess) {
+        *err = e;
+        return true;
+    }
+    const int slots = cus * (per_cu > 0 ? per_cu : 1);
+    const dim3 grid((unsigned)(g.groups < slots ? g.groups : slots)), block(64 * SPLIT);
+    kernel<<<grid, block, lds, stream>>>(x, qweight, scales, zeros, y, g);
     *err = hipGetLastError();
     return true;
 }
@@ -1102,6 +1488,12 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
             if (kblocks >= 64) Q4_PAIR(4, 2, 2, 2);
             Q4_RES(4, 2, 1, 2);
         } else {
+            // many tile groups (n_out of 32768 and more): persistent
+            // workgroups stage x once each and walk several groups
+            if (tiles >= 2048 && m <= 8 &&
+                plan_persistent<8, 4, 2, 1, FOLD, 4, true>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y,
+                                                           stream, query, &e))
+                return e;
             if (tiles >= 640) Q4_PAIR(8, 4, 2, 1);
             if (tiles >= 256) Q4_RES(8, 2, 1, 2);
             Q4_RES(8, 1, 1, 2);
