@@ -942,6 +942,12 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_persistent_kernel(
     const char *xrow = x_lds + min(col, m - 1) * geo.x_row_bytes;
     const uint32_t *szrow = sz_lds + col * geo.sz_stride;
     for (;;) {
+        // the next group's first batch of scale|zero pairs is requested
+        // before this group's weights, so waiting for it at the group
+        // boundary leaves the ring's prefetched stages in flight
+        const bool has_next = ntg < ngroups;
+        const int nrow0 = ntg * ROWS;
+        if (has_next) sz_load(nrow0, tid, s8, z8);
         f32x4 acc[CT];
 #pragma unroll
         for (int t = 0; t < CT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -982,17 +988,14 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_persistent_kernel(
         }
         // nstages is a multiple of DEPTH (the planner checks it), so slot d
         // now holds stage d of the next group
-        const bool has_next = ntg < ngroups;
-        const int nrow0 = ntg * ROWS;
-        if (has_next) sz_load(nrow0, tid, s8, z8);
-        __syncthreads();                                  // every wave is done with the pairs
+        barrier_keep_vmem();                              // every wave is done with the pairs
         const int col_n = row0 + col;
         if (SPLIT > 1) {
             if (lane < 32) {
 #pragma unroll
                 for (int t = 0; t < CT; ++t) part[(wave * CT + t) * 32 + lane] = acc[t];
             }
-            __syncthreads();
+            barrier_keep_vmem();
             if (wave < CT && lane < 32) {
                 const int t = wave;
                 f32x4 sum = part[t * 32 + lane];
@@ -1020,13 +1023,13 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_persistent_kernel(
             }
         }
         if (!has_next) break;
-        __syncthreads();                                  // the partial sums have been read
+        barrier_keep_vmem();                              // the partial sums have been read
         sz_store(nrow0, tid, s8, z8);
         for (int c = tid + THREADS; c < sz_units(nrow0); c += THREADS) {
             sz_load(nrow0, c, s8, z8);
             sz_store(nrow0, c, s8, z8);
         }
-        __syncthreads();
+        barrier_keep_vmem();
         tg = ntg;
         row0 = nrow0;
         ntg = tg + (int)gridDim.x;
