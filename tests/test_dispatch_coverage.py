@@ -89,7 +89,7 @@ def test_profiled_kernels_are_covered(covered):
     """Every q4_gemv / q4_gemm instantiation named in a committed profile
     summary is one the parity tests run (a stale profile fails here)."""
     pat = re.compile(r"\b(gemv_resident_kernel|gemv_window_kernel|gemv_rowstream_kernel|gemv_persistent_kernel|"
-                     r"gemv_stream_kernel|gemm_kernel)<[^<>]*>")
+                     r"gemm_kernel)<[^<>]*>")
     seen = set()
     for path in glob.glob(os.path.join(ROOT, "profiles", "*")):
         with open(path, encoding="utf-8") as f:
