@@ -26,20 +26,21 @@ COVERAGE = [Case(*c) for c in (
     ("gemm", 8, 300, 100, 2048, 128, 258),     # gemm_kernel<256, 128, 8, true, 1> (2-byte aligned metadata: per-step gathers)
     ("gemm", 8, 17, 17, 128, 64, 256),         # gemm_kernel<256, 128, 8, true, 2>
     ("gemm", 8, 17, 17, 1024, 64, 256),        # gemm_kernel<256, 128, 8, true, 8>
+    ("gemv", 4, 3, 32777, 2048, 128, 256),     # gemv_persistent_kernel<8, 4, 2, 1, true, true> (ragged last group)
+    ("gemv", 4, 8, 32800, 4096, 256, 256),     # gemv_persistent_kernel<8, 4, 2, 1, true, true> (groups of 256)
     ("gemv", 4, 2, 17, 2016, 32, 256),         # gemv_resident_kernel<16, 1, 1, 4, false, 4, false>
     ("gemv", 4, 1, 8192, 16416, 32, 256),      # gemv_resident_kernel<16, 1, 2, 1, false, 4, true>
     ("gemv", 4, 2, 17, 32, 32, 256),           # gemv_resident_kernel<4, 1, 1, 2, false, 4, false>
     ("gemv", 8, 2, 17, 32, 32, 256),           # gemv_resident_kernel<4, 1, 1, 2, false, 8, false>
-    ("gemv", 8, 1, 4112, 2016, 32, 256),       # gemv_resident_kernel<4, 1, 1, 2, false, 8, true>
+    ("gemv", 8, 1, 4112, 2016, 32, 258),       # gemv_resident_kernel<4, 1, 1, 2, false, 8, true> (2-byte aligned metadata)
     ("gemv", 4, 2, 17, 128, 128, 256),         # gemv_resident_kernel<4, 1, 1, 2, true, 4, false>
-    ("gemv", 8, 1, 12304, 2016, 32, 256),      # gemv_resident_kernel<4, 2, 1, 1, false, 8, true>
-    ("gemv", 4, 1, 12304, 2016, 2016, 256),    # gemv_resident_kernel<4, 2, 1, 2, false, 4, false>
+    ("gemv", 8, 1, 12304, 2016, 32, 258),      # gemv_resident_kernel<4, 2, 1, 1, false, 8, true> (2-byte aligned metadata)
+    ("gemv", 4, 1, 12304, 2016, 32, 258),      # gemv_resident_kernel<4, 2, 1, 2, false, 4, false> (2-byte aligned metadata)
     ("gemv", 4, 1, 12304, 2048, 128, 258),     # gemv_resident_kernel<4, 2, 1, 2, true, 4, false> (2-byte aligned metadata)
     ("gemv", 4, 1, 12304, 8192, 128, 258),     # gemv_resident_kernel<4, 2, 2, 2, true, 4, true> (2-byte aligned metadata)
-    ("gemv", 4, 1, 17, 2016, 2016, 256),       # gemv_resident_kernel<8, 1, 1, 2, false, 4, false>
     ("gemv", 4, 1, 17, 2016, 32, 258),         # gemv_resident_kernel<8, 1, 1, 2, false, 4, false> (2-byte aligned metadata: no row-streaming kernel)
     ("gemv", 8, 2, 17, 2016, 32, 256),         # gemv_resident_kernel<8, 1, 1, 2, false, 8, false>
-    ("gemv", 8, 1, 17, 2016, 32, 256),         # gemv_resident_kernel<8, 1, 1, 2, false, 8, true>
+    ("gemv", 8, 1, 17, 2016, 32, 258),         # gemv_resident_kernel<8, 1, 1, 2, false, 8, true> (2-byte aligned metadata)
     ("gemv", 4, 2, 17, 2048, 128, 256),        # gemv_resident_kernel<8, 1, 1, 2, true, 4, false>
     ("gemv", 4, 1, 17, 16416, 32, 256),        # gemv_resident_kernel<8, 1, 1, 3, false, 4, false>
     ("gemv", 8, 1, 17, 16416, 32, 256),        # gemv_resident_kernel<8, 1, 1, 3, false, 8, true>
@@ -48,7 +49,20 @@ COVERAGE = [Case(*c) for c in (
     ("gemv", 4, 2, 4096, 2048, 128, 256),      # gemv_resident_kernel<8, 2, 1, 2, true, 4, false>
     ("gemv", 8, 5, 10240, 2016, 32, 256),      # gemv_resident_kernel<8, 4, 1, 1, false, 8, true>
     ("gemv", 4, 2, 10240, 2048, 128, 256),     # gemv_resident_kernel<8, 4, 2, 1, true, 4, true>
+    ("gemv", 8, 1, 17, 32, 32, 256),           # gemv_rowstream8_kernel<1, 8>
+    ("gemv", 8, 1, 17, 13312, 256, 256),       # gemv_rowstream8_kernel<13, 8>
+    ("gemv", 8, 1, 1003, 16384, 16384, 256),   # gemv_rowstream8_kernel<16, 8> (per-channel, ragged rows)
+    ("gemv", 8, 1, 17, 2016, 32, 256),         # gemv_rowstream8_kernel<2, 8>
+    ("gemv", 8, 1, 4112, 2016, 32, 256),       # gemv_rowstream8_kernel<2, 8>
+    ("gemv", 8, 1, 12304, 2016, 32, 256),      # gemv_rowstream8_kernel<2, 8>
+    ("gemv", 8, 1, 17, 2080, 32, 256),         # gemv_rowstream8_kernel<3, 8>
+    ("gemv", 8, 1, 17, 4224, 64, 256),         # gemv_rowstream8_kernel<5, 8>
+    ("gemv", 8, 1, 17, 8192, 128, 256),        # gemv_rowstream8_kernel<8, 8>
+    ("gemv", 8, 1, 17, 8320, 32, 256),         # gemv_rowstream8_kernel<9, 8>
+    ("gemv", 8, 1, 517, 8320, 8320, 256),      # gemv_rowstream8_kernel<9, 8> (per-channel, n_in not a power of two)
+    ("gemv", 4, 1, 17, 2016, 2016, 256),       # gemv_rowstream_kernel<1, 1, 8> (per-channel)
     ("gemv", 4, 1, 17, 2016, 32, 256),         # gemv_rowstream_kernel<1, 1, 8>
+    ("gemv", 4, 1, 12304, 2016, 2016, 256),    # gemv_rowstream_kernel<1, 1, 8> (per-channel)
     ("gemv", 4, 1, 12304, 2016, 32, 256),      # gemv_rowstream_kernel<1, 1, 8>
     ("gemv", 4, 1, 12304, 2048, 128, 256),     # gemv_rowstream_kernel<1, 1, 8>
     ("gemv", 4, 1, 17, 4224, 32, 256),         # gemv_rowstream_kernel<3, 1, 8>
@@ -59,8 +73,6 @@ COVERAGE = [Case(*c) for c in (
     ("gemv", 4, 1, 12301, 8320, 128, 256),     # gemv_rowstream_kernel<5, 1, 8> (ragged rows, odd group count, partial chunk)
     ("gemv", 4, 1, 1000, 13312, 32, 256),      # gemv_rowstream_kernel<7, 1, 8> (partial last chunk of 2048)
     ("gemv", 4, 1, 8192, 16384, 128, 256),     # gemv_rowstream_kernel<8, 1, 8>
-    ("gemv", 4, 3, 32777, 2048, 128, 256),     # gemv_persistent_kernel<8, 4, 2, 1, true, true> (ragged last group)
-    ("gemv", 4, 8, 32800, 4096, 256, 256),     # gemv_persistent_kernel<8, 4, 2, 1, true, true> (groups of 256)
     ("gemv", 4, 4, 17, 16416, 32, 256),        # gemv_window_kernel<16, 2, 1, false, 8, 4>
     ("gemv", 8, 4, 17, 16416, 32, 256),        # gemv_window_kernel<16, 2, 1, false, 8, 8>
     ("gemv", 4, 5, 17, 16384, 128, 256),       # gemv_window_kernel<16, 2, 1, true, 8, 4>

@@ -67,9 +67,9 @@
 //  * windowed: for larger m * n_in, x and scale|zero pairs are staged one
 //    window (one stage of blocks) ahead in double-buffered LDS, with one
 //    barrier per window.
-// and, for m = 1 with grouped INT4 rows of up to 16384 codes, the
-// row-streaming kernel (one wave per row, VALU dot products), described
-// where it is defined.
+// and, for m = 1 with rows of up to 16384 codes, the row-streaming kernels
+// (one wave per row, VALU dot products; INT4 and INT8), described where
+// they are defined.
 // Loads past the last block are redirected to x (hot in L2) rather than
 // re-reading weights, so no load is conditional and the compiler keeps the
 // ring in flight.  Partial results of the SPLIT waves are summed in LDS in a
@@ -553,7 +553,8 @@ __global__ __launch_bounds__(64 * SPLIT) void gemv_resident_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Row-streaming kernel (m = 1, INT4, groups of 32 to 256, n_in <= 16384).
+// Row-streaming kernel (m = 1, INT4, groups of at least 32 codes or one per
+// row, n_in <= 16384).
 //
 // Every load instruction of a wave reads one contiguous KiB of one row (2048
 // codes; lane l holds codes 32l .. 32l + 31 of the chunk), the access pattern
@@ -730,6 +731,118 @@ __global__ __launch_bounds__(64 * W) void gemv_rowstream_kernel(
         const float t = wave_sum(acc[r]);
         if (lane == r && row0 + r < n_out) y[row0 + r] = bitcast<uint16_t>((_Float16)t);
     }
+}
+
+// Row streaming for INT8 weights (m = 1, any group: 32..256 or one per
+// row): a load instruction of a wave reads one contiguous KiB of its row
+// (lane l: codes 16l .. 16l + 15 of a 1024-code chunk); masking a word with
+// 0x00FF00FF leaves the byte codes (c0, c2) as the fp16 subnormals c 2^-24,
+// the word shifted by 8 gives (c1, c3), and x is pre-permuted into the
+// matching pairs.  A lane's 16 codes lie in one group (groups have at least
+// 32 codes), so its scale and zero-point are applied once per chunk:
+// y += s 2^24 (A - z X24), the cancellation between A and z X24 confined to
+// 16 terms.  Each chunk's x is read from LDS where it is used (48-byte lane
+// slots: 32 of x, padding against bank conflicts).
+constexpr int kRs8Slot = 48;
+
+template <int NC, int W>
+__global__ __launch_bounds__(64 * W) void gemv_rowstream8_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    uint16_t *__restrict__ y, Geometry geo)
+{
+    constexpr int THREADS = 64 * W;
+    constexpr int XP = NC * 128;          // 16-byte pieces of x (past n_in they read as 0)
+    constexpr int XI = (XP + THREADS - 1) / THREADS;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+
+    const int n_out = geo.n_out, n_in = geo.n_in, G = geo.groups_per_row, gshift = geo.group_shift;
+    char *x_lds = lds;                                                    // [NC * 64][kRs8Slot]
+    float *xs_lds = reinterpret_cast<float *>(lds + NC * 64 * kRs8Slot);  // [NC * 64]
+    uint16_t *s_lds = reinterpret_cast<uint16_t *>(xs_lds + NC * 64);     // [W][G]
+    uint16_t *z_lds = s_lds + ((W * G + 7) & ~7);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg_row0 = blockIdx.x * W, row = wg_row0 + wave;
+    const int row_bytes = n_in;
+
+    const int meta = min(W, n_out - wg_row0) * G * 2;
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(scales + (int64_t)wg_row0 * G), (short)0, meta, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(zeros + (int64_t)wg_row0 * G), (short)0, meta, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x), (short)0, n_in * 2, kBufferFlags);
+    const int n_vec = (W * G * 2 + 15) >> 4;
+    const u32x4 sv = meta_vec(sr, tid * 16, meta);
+    const u32x4 zv = meta_vec(zr, tid * 16, meta);
+    u32x4 xv[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (tid + i * THREADS) * 16, 0, 0);
+
+    // the row's chunks: rows past n_out read the last row, lanes past the end
+    // of a row its last 16 bytes (their x is 0); neither is stored
+    const char *wrow = reinterpret_cast<const char *>(qweight) + (int64_t)min(row, n_out - 1) * row_bytes;
+    u32x4 ring[NC];
+#pragma unroll
+    for (int h = 0; h < NC; ++h) {
+        const uint32_t off = min((uint32_t)(1024 * h + 16 * lane), (uint32_t)row_bytes - 16u);
+        ring[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + off));
+    }
+
+    if (tid < n_vec) {
+        reinterpret_cast<u32x4 *>(s_lds)[tid] = sv;
+        reinterpret_cast<u32x4 *>(z_lds)[tid] = zv;
+    }
+    for (int v = tid + THREADS; v < n_vec; v += THREADS) {
+        reinterpret_cast<u32x4 *>(s_lds)[v] = meta_vec(sr, v * 16, meta);
+        reinterpret_cast<u32x4 *>(z_lds)[v] = meta_vec(zr, v * 16, meta);
+    }
+    // piece p holds x[8p .. 8p + 7]; slot p / 2 is (chunk, lane), its two
+    // pieces in neighbouring lanes, whose pair sum gives X24
+    const uint32_t ones = 0x3C003C00u;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int p = tid + i * THREADS;
+        u32x4 pp;
+        pp[0] = __builtin_amdgcn_perm(xv[i][1], xv[i][0], 0x05040100u);      // (x0, x2)
+        pp[1] = __builtin_amdgcn_perm(xv[i][1], xv[i][0], 0x07060302u);      // (x1, x3)
+        pp[2] = __builtin_amdgcn_perm(xv[i][3], xv[i][2], 0x05040100u);      // (x4, x6)
+        pp[3] = __builtin_amdgcn_perm(xv[i][3], xv[i][2], 0x07060302u);      // (x5, x7)
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t = dot2_f16(pp[e], ones, t);
+        t += dpp_f32<0xB1>(t);
+        if (p < XP) {
+            *reinterpret_cast<u32x4 *>(x_lds + (p >> 1) * kRs8Slot + (p & 1) * 16) = pp;
+            if ((p & 1) == 0) xs_lds[p >> 1] = t * 5.9604644775390625e-08f;   // 2^-24
+        }
+    }
+    barrier_keep_vmem();
+
+    float acc = 0.f;
+#pragma unroll
+    for (int h = 0; h < NC; ++h) {
+        const u32x4 w = ring[h];
+        const u32x4 xa = *reinterpret_cast<const u32x4 *>(x_lds + (h * 64 + lane) * kRs8Slot);
+        const u32x4 xb = *reinterpret_cast<const u32x4 *>(x_lds + (h * 64 + lane) * kRs8Slot + 16);
+        const float x24 = xs_lds[h * 64 + lane];
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 &xp = j < 2 ? xa : xb;
+            const uint32_t v = w[j];
+            a = dot2_f16(v & 0x00FF00FFu, xp[(j & 1) * 2], a);             // codes 4j, 4j+2
+            a = dot2_f16((v >> 8) & 0x00FF00FFu, xp[(j & 1) * 2 + 1], a);  // 4j+1, 4j+3
+        }
+        const int e = wave * G + min((1024 * h + 16 * lane) >> gshift, G - 1);
+        const float s = half_bits_to_float(s_lds[e]) * 16777216.0f;      // s 2^24, exact
+        const float z = half_bits_to_float(z_lds[e]);
+        acc = __builtin_fmaf(s, __builtin_fmaf(-z, x24, a), acc);
+    }
+    const float t = wave_sum(acc);
+    if (lane == 0 && row < n_out) y[row] = bitcast<uint16_t>((_Float16)t);
 }
 
 // ---------------------------------------------------------------------------
@@ -1277,10 +1390,10 @@ bool plan_rowstream(const uint16_t *x, const uint32_t *qweight, const uint16_t *
                     uint16_t *y, hipStream_t stream, const char **query, hipError_t *err)
 {
     static_assert(RW == 1 || RW == 2 || RW == 4 || RW == 8, "one storing lane per row");
-    // m = 1, groups of 32 to 256 codes, NC chunks of 2048 codes per row, and
-    // scale and zero-point arrays the staging reads as 4-byte words
-    if (m != 1 || group_shift < 5 || group_shift > 8 || (n_in & 31) != 0 || (n_in + 2047) / 2048 != NC)
-        return false;
+    // m = 1, groups of at least 32 codes (or one per row), NC chunks of 2048
+    // codes per row, and scale and zero-point arrays the staging reads as
+    // 4-byte words
+    if (m != 1 || group_shift < 5 || (n_in & 31) != 0 || (n_in + 2047) / 2048 != NC) return false;
     if (((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 3) != 0) return false;
     Geometry g = make_geometry(m, n_out, n_in, group_shift, 4);
     constexpr int R = W * RW;
@@ -1302,6 +1415,38 @@ bool plan_rowstream(const uint16_t *x, const uint32_t *qweight, const uint16_t *
         }
     }
     kernel<<<dim3((unsigned)((n_out + R - 1) / R)), dim3(64 * W), lds, stream>>>(x, qweight, scales, zeros, y, g);
+    *err = hipGetLastError();
+    return true;
+}
+
+template <int NC, int W>
+bool plan_rowstream8(const uint16_t *x, const uint32_t *qweight, const uint16_t *scales,
+                     const uint16_t *zeros, int m, int n_out, int n_in, int group_shift,
+                     uint16_t *y, hipStream_t stream, const char **query, hipError_t *err)
+{
+    // m = 1, groups of at least 32 codes (or one per row), NC chunks of 1024
+    // codes per row, and scale and zero-point arrays the staging reads as
+    // 4-byte words
+    if (m != 1 || group_shift < 5 || (n_in & 31) != 0 || (n_in + 1023) / 1024 != NC) return false;
+    if (((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 3) != 0) return false;
+    Geometry g = make_geometry(m, n_out, n_in, group_shift, 8);
+    const size_t lds = (size_t)NC * 64 * (kRs8Slot + 4) + 2 * (size_t)((W * g.groups_per_row + 7) & ~7) * 2;
+    if (lds > kMaxLds) return false;
+    *err = hipSuccess;
+    if (query) {
+        static const std::string name = "gemv_rowstream8_kernel<" + std::to_string(NC) + ", " + std::to_string(W) + ">";
+        *query = name.c_str();
+        return true;
+    }
+    auto kernel = gemv_rowstream8_kernel<NC, W>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = allow_full_lds(kernel);
+        if (e != hipSuccess) {
+            *err = e;
+            return true;
+        }
+    }
+    kernel<<<dim3((unsigned)((n_out + W - 1) / W)), dim3(64 * W), lds, stream>>>(x, qweight, scales, zeros, y, g);
     *err = hipGetLastError();
     return true;
 }
@@ -1424,10 +1569,11 @@ bool plan_window(const uint16_t *x, const uint32_t *qweight, const uint16_t *sca
 
 // Configurations chosen from measured sweeps on MI355X over the decode
 // shapes (7B and 70B projections, m = 1 and 8, INT4 and INT8); other shapes
-// fall through to the nearest rule.  One row of x with grouped INT4 weights
-// takes the row-streaming kernel (14-31 % faster than the MFMA kernels on
-// every such shape swept, 4096 to 16384 codes per row) unless the scale or
-// zero-point array is only 2-byte aligned or rows are longer than 16384.  Paired INT4 loads pay on rows of 8192
+// fall through to the nearest rule.  One row of x takes the row-streaming
+// kernels (INT4 14-31 %, INT8 12-32 % faster than the MFMA kernels on every
+// such shape swept, 4096 to 16384 codes per row, grouped or per-channel)
+// unless the scale or zero-point array is only 2-byte aligned or rows are
+// longer than 16384 codes.  Paired INT4 loads pay on rows of 8192
 // codes and more (9-26 % on the 70B and 8192x28672 shapes); on the
 // 4096-wide 7B linears, whose launches are short and dependent, they
 // measured the same as the fragment-order loads, which are kept there.
@@ -1452,12 +1598,22 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
     case NC: \
         if (plan_rowstream<NC, 1, 8>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e; \
         break
-    if constexpr (BITS == 4) {
-        // one token, grouped INT4 rows of up to 16384 codes: one wave per row
-        // (8 rows per workgroup measured best on every such shape swept)
-        if (m == 1) {
+#define Q8_RS(NC) \
+    case NC: \
+        if (plan_rowstream8<NC, 8>(x, qweight, scales, zeros, m, n_out, n_in, group_shift, y, stream, query, &e)) return e; \
+        break
+    // one token and rows of up to 16384 codes: one wave per row (8 rows per
+    // workgroup measured best on every such shape swept)
+    if (m == 1) {
+        if constexpr (BITS == 4) {
             switch ((n_in + 2047) / 2048) {
                 Q4_RS(1); Q4_RS(2); Q4_RS(3); Q4_RS(4); Q4_RS(5); Q4_RS(6); Q4_RS(7); Q4_RS(8);
+            default: break;
+            }
+        } else {
+            switch ((n_in + 1023) / 1024) {
+                Q8_RS(1); Q8_RS(2); Q8_RS(3); Q8_RS(4); Q8_RS(5); Q8_RS(6); Q8_RS(7); Q8_RS(8);
+                Q8_RS(9); Q8_RS(10); Q8_RS(11); Q8_RS(12); Q8_RS(13); Q8_RS(14); Q8_RS(15); Q8_RS(16);
             default: break;
             }
         }
@@ -1510,6 +1666,7 @@ hipError_t dispatch(const uint16_t *x, const uint32_t *qweight, const uint16_t *
 #undef Q4_PAIR
 #undef Q4_WIN
 #undef Q4_RS
+#undef Q8_RS
     return hipErrorInvalidValue;                // unreachable: the last window always fits
 }
 
