@@ -56,6 +56,7 @@ COVERAGE = [Case(*c) for c in (
     ("gemv", 8, 1, 4112, 2016, 32, 256),       # gemv_rowstream8_kernel<2, 8>
     ("gemv", 8, 1, 12304, 2016, 32, 256),      # gemv_rowstream8_kernel<2, 8>
     ("gemv", 8, 1, 17, 2080, 32, 256),         # gemv_rowstream8_kernel<3, 8>
+    ("gemv", 8, 1, 1003, 4096, 4096, 260),     # gemv_rowstream8_kernel<4, 8> (per-channel, 4-byte aligned metadata)
     ("gemv", 8, 1, 17, 4224, 64, 256),         # gemv_rowstream8_kernel<5, 8>
     ("gemv", 8, 1, 17, 8192, 128, 256),        # gemv_rowstream8_kernel<8, 8>
     ("gemv", 8, 1, 17, 8320, 32, 256),         # gemv_rowstream8_kernel<9, 8>
@@ -67,6 +68,7 @@ COVERAGE = [Case(*c) for c in (
     ("gemv", 4, 1, 12304, 2048, 128, 256),     # gemv_rowstream_kernel<1, 1, 8>
     ("gemv", 4, 1, 17, 4224, 32, 256),         # gemv_rowstream_kernel<3, 1, 8>
     ("gemv", 4, 1, 4101, 6144, 256, 256),      # gemv_rowstream_kernel<3, 1, 8> (groups of 256, ragged rows)
+    ("gemv", 4, 1, 4101, 6144, 128, 260),      # gemv_rowstream_kernel<3, 1, 8> (4-byte aligned metadata)
     ("gemv", 4, 1, 17, 8192, 128, 256),        # gemv_rowstream_kernel<4, 1, 8>
     ("gemv", 4, 1, 12304, 8192, 128, 256),     # gemv_rowstream_kernel<4, 1, 8>
     ("gemv", 4, 1, 17, 8320, 32, 256),         # gemv_rowstream_kernel<5, 1, 8>
