@@ -218,6 +218,26 @@ def time_graph(graph, steps, warmup):
     return start.elapsed_time(end) * 1e-3, wall
 
 
+def replay_percentiles(graph, replays, scale=1.0):
+    """p10 / p50 / p90 of single graph replays, each bracketed by its own pair
+    of HIP events (a separate pass after the headline timing, which stays one
+    bracket over all its steps); `scale` converts a replay's seconds into the
+    reported unit."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(replays):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e-3 * scale for i in range(replays))
+
+    def q(f):
+        return round(t[min(len(t) - 1, int(f * len(t)))], 4)
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "replays": replays}
+
+
 def settle(graph, seconds=0.25):
     """Untimed replays for at least `seconds`: under MFMA load the clock settles
     at its loaded value only after some 0.1 s, and the first replays after a
@@ -322,7 +342,8 @@ def bench_decode(args, dev, host):
                ms_per_step=elapsed / args.steps * 1e3,
                gbs=step_bytes * args.steps / elapsed / 1e9,
                per_launch_us=per_launch_s * 1e6,
-               bytes_per_launch=step_bytes / launches)
+               bytes_per_launch=step_bytes / launches,
+               ms_per_step_percentiles=replay_percentiles(graph, max(10, args.steps), 1e3))
     # The same weights with one launch per linear (7 per layer): row slices
     # of the fused matrices are themselves valid packed weights.
     res["gbs_7_launches_per_layer"] = None
@@ -360,7 +381,8 @@ def bench_prefill(args, dev, bits=4):
         t = el / (5 * reps)
         flop = 2 * syn.PREFILL_M * lin.n_out * lin.n_in
         out.append(dict(shape=f"{syn.PREFILL_M}x{lin.n_out}x{lin.n_in}", us=round(t * 1e6, 2),
-                        tflops=round(flop / t / 1e12, 1)))
+                        tflops=round(flop / t / 1e12, 1),
+                        us_percentiles=replay_percentiles(g, 10, 1e6 / reps)))
         tot_flop += flop
         tot_t += t
         del qw, x, y, g
@@ -388,10 +410,11 @@ def bench_decode70b(args, dev):
     torch.cuda.synchronize()
     log(f"70B stack: {layers} layers quantized in {time.perf_counter() - t0:.1f} s")
     g = capture(lambda: [gemv(x, qw, y) for qw, x, y in gemvs])
-    el, _ = time_graph(g, 5, 1)
+    el, _ = time_graph(g, 5, 3)
     nbytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 8, 128) for qw, _, _ in gemvs)
     res = dict(layers=layers, m=8, gemvs_per_pass=len(gemvs), ms_per_pass=round(el / 5 * 1e3, 3),
-               gbs=round(nbytes * 5 / el / 1e9, 1), resident_gb=round(nbytes / 1e9, 2))
+               gbs=round(nbytes * 5 / el / 1e9, 1), resident_gb=round(nbytes / 1e9, 2),
+               ms_per_pass_percentiles=replay_percentiles(g, 5, 1e3))
     del gemvs, g
     torch.cuda.empty_cache()
     return res
@@ -935,6 +958,7 @@ def main():
                      "bytes_per_launch": round(decode["bytes_per_launch"])},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(decode["wall"], 4),
+        "ms_per_step_percentiles": decode["ms_per_step_percentiles"],
         "decode_7_launches_per_layer_gbs": decode["gbs_7_launches_per_layer"],
     }
     if "prefill" in extras:
