@@ -343,7 +343,8 @@ def bench_decode(args, dev, host):
                gbs=step_bytes * args.steps / elapsed / 1e9,
                per_launch_us=per_launch_s * 1e6,
                bytes_per_launch=step_bytes / launches,
-               ms_per_step_percentiles=replay_percentiles(graph, max(10, args.steps), 1e3))
+               ms_per_step_percentiles=None if args.decode_only else
+               replay_percentiles(graph, max(10, args.steps), 1e3))
     # The same weights with one launch per linear (7 per layer): row slices
     # of the fused matrices are themselves valid packed weights.
     res["gbs_7_launches_per_layer"] = None
@@ -414,7 +415,7 @@ def bench_decode70b(args, dev):
     nbytes = sum(algorithmic_bytes(qw.n_out, qw.n_in, 8, 128) for qw, _, _ in gemvs)
     res = dict(layers=layers, m=8, gemvs_per_pass=len(gemvs), ms_per_pass=round(el / 5 * 1e3, 3),
                gbs=round(nbytes * 5 / el / 1e9, 1), resident_gb=round(nbytes / 1e9, 2),
-               ms_per_pass_percentiles=replay_percentiles(g, 5, 1e3))
+               ms_per_pass_percentiles=None if args.decode70b_only else replay_percentiles(g, 5, 1e3))
     del gemvs, g
     torch.cuda.empty_cache()
     return res
@@ -847,6 +848,9 @@ def main():
                          "used for profiling")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill GEMM phase, printed as its own JSON line; used for profiling")
+    ap.add_argument("--decode70b-only", action="store_true",
+                    help="only the 70B-shaped m=8 pass (timed replays, no percentile pass), printed as its own "
+                         "JSON line; used for profiling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one elementwise copy of 256 MiB (268435456 bytes read and written), "
                          "the known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -897,6 +901,16 @@ def main():
             "prefill": pre, "roofline": {"bound": "mfma", "achieved": pre["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
                                          "unit": "TFLOP/s", "frac": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4)}}),
               flush=True)
+        return
+    if args.decode70b_only:
+        res = bench_decode70b(args, dev)
+        check_calls()
+        log(f"decode70b: {res}")
+        print(json.dumps({"metric": "W4A16 decode GEMV HBM GB/s, 70B-shaped pass at m=8", "value": res["gbs"],
+                          "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
+                          "config": {"workload": "Llama-2-70B-shaped decode, m=8: 80 layers x 4 fused GEMVs, "
+                                                 "INT4 g=128"},
+                          "decode70b": res}), flush=True)
         return
     if args.decode_only:
         args.no_extras = True
