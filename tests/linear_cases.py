@@ -49,6 +49,7 @@ COVERAGE = [Case(*c) for c in (
     ("gemv", 4, 2, 4096, 2048, 128, 256),      # gemv_resident_kernel<8, 2, 1, 2, true, 4, false>
     ("gemv", 8, 5, 10240, 2016, 32, 256),      # gemv_resident_kernel<8, 4, 1, 1, false, 8, true>
     ("gemv", 4, 2, 10240, 2048, 128, 256),     # gemv_resident_kernel<8, 4, 2, 1, true, 4, true>
+    ("gemv", 8, 1, 9, 64, 64, 256),            # gemv_rowstream8_kernel<1, 8> (per-channel, 64-code rows)
     ("gemv", 8, 1, 17, 32, 32, 256),           # gemv_rowstream8_kernel<1, 8>
     ("gemv", 8, 1, 17, 13312, 256, 256),       # gemv_rowstream8_kernel<13, 8>
     ("gemv", 8, 1, 1003, 16384, 16384, 256),   # gemv_rowstream8_kernel<16, 8> (per-channel, ragged rows)
@@ -61,8 +62,10 @@ COVERAGE = [Case(*c) for c in (
     ("gemv", 8, 1, 17, 8192, 128, 256),        # gemv_rowstream8_kernel<8, 8>
     ("gemv", 8, 1, 17, 8320, 32, 256),         # gemv_rowstream8_kernel<9, 8>
     ("gemv", 8, 1, 517, 8320, 8320, 256),      # gemv_rowstream8_kernel<9, 8> (per-channel, n_in not a power of two)
+    ("gemv", 4, 1, 9, 64, 32, 256),            # gemv_rowstream_kernel<1, 1, 8> (two-lane rows)
     ("gemv", 4, 1, 17, 2016, 2016, 256),       # gemv_rowstream_kernel<1, 1, 8> (per-channel)
     ("gemv", 4, 1, 17, 2016, 32, 256),         # gemv_rowstream_kernel<1, 1, 8>
+    ("gemv", 4, 1, 17, 32, 32, 256),           # gemv_rowstream_kernel<1, 1, 8> (one 32-code row)
     ("gemv", 4, 1, 12304, 2016, 2016, 256),    # gemv_rowstream_kernel<1, 1, 8> (per-channel)
     ("gemv", 4, 1, 12304, 2016, 32, 256),      # gemv_rowstream_kernel<1, 1, 8>
     ("gemv", 4, 1, 12304, 2048, 128, 256),     # gemv_rowstream_kernel<1, 1, 8>
