@@ -115,3 +115,14 @@ def test_config_query_validates_like_the_entry_points():
     small = ctypes.create_string_buffer(8)
     assert L.q4_linear_config(0, 4, 1, 64, 128, 128, 256, 256, small, 8) == 0
     assert len(small.value) == 7                       # truncated, NUL-terminated
+
+
+def test_one_token_bench_calls_take_row_streaming():
+    """The benchmark's m = 1 GEMVs (INT4 grouped, INT8 per-channel) run on the
+    row-streaming kernels; a dispatch change that sent them back to the MFMA
+    kernels would cost 12-31 % per launch."""
+    calls = [c for c in bench_cases() if c.kind == "gemv" and c.m == 1 and c.n_in <= 16384]
+    assert calls
+    for c in calls:
+        name = config(c)
+        assert name.startswith("gemv_rowstream"), f"{c}: {name}"
